@@ -1,0 +1,322 @@
+#!/usr/bin/env python3
+"""Throughput of the MoE dispatch / combine hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config prefill]
+
+One step = the whole forward hot path over one batch of the workload:
+dispatch layout -> FP8 dispatch (pack + quantize) -> combine (weighted
+gather-reduce to bf16), all inputs resident in HBM. `value` is dispatch +
+combine algorithmic bytes per second of step time (GB/s); the JSON line also
+carries the per-kernel breakdown, the roofline of the dominant kernel, the
+decode latency at 128 tokens, the backward pair, and the CPU oracle baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--config", default="prefill")
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-extras", action="store_true", help="skip decode/backward/copy extras")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    return p.parse_args()
+
+
+def algo_bytes(T, k, H, N, use_fp8):
+    """Bytes the method must move (kept slots N): reads of x and weights and
+    positions, writes of the rows, scales and received weights; combine reads
+    the rows and writes y."""
+    G = H // 128
+    if use_fp8:
+        d = 2 * T * H + N * H + 4 * N * G + 4 * N + 8 * T * k
+    else:
+        d = 2 * T * H + 2 * N * H + 4 * N + 8 * T * k
+    c = 2 * N * H + 2 * T * H + 8 * T * k
+    cb = 2 * T * H + 2 * N * H + 4 * T * k
+    return d, c, cb
+
+
+class Path:
+    """Device buffers and the step of one workload (everything preallocated)."""
+
+    def __init__(self, cfg, seed, torch, ep, workloads):
+        self.cfg = cfg
+        self.torch = torch
+        wl = workloads.make_workload(cfg, seed=seed)
+        self.wl = wl
+        dev = "cuda"
+        self.x = torch.from_numpy(wl.x.view("int16")).to(dev).view(torch.bfloat16)
+        self.topk = torch.from_numpy(wl.topk_idx).to(dev)
+        self.w = torch.from_numpy(wl.topk_w).to(dev)
+        # receive capacity: the largest per-rank row count (one layout on a
+        # provisional context, outside any timing)
+        probe = ep.Buffer(cfg.T, cfg.H, cfg.k, cfg.E, cfg.R, cfg.T * cfg.k)
+        Lp = probe.get_dispatch_layout(self.topk)
+        self.cap = int(Lp.rank_rows.max().item()) if cfg.T else 0
+        probe.status()
+        probe.close()
+        self.buf = ep.Buffer(cfg.T, cfg.H, cfg.k, cfg.E, cfg.R, self.cap)
+        b = self.buf
+        self.layout = b.new_layout()
+        n = b.num_rows
+        self.recv_x = torch.empty((n, cfg.H), dtype=torch.uint8 if cfg.use_fp8 else torch.bfloat16, device=dev)
+        self.recv_scales = torch.empty((n, cfg.H // 128), dtype=torch.float32, device=dev) if cfg.use_fp8 else None
+        self.recv_w = torch.empty(n, dtype=torch.float32, device=dev)
+        self.handle = b.new_handle()
+        self.expert_out = workloads.device_normal_bf16((n, cfg.H), seed=seed + 101)
+        self.y = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device=dev)
+        self.grad_y = None
+
+    def layout_op(self):
+        self.buf.get_dispatch_layout(self.topk, self.layout)
+
+    def dispatch_op(self):
+        self.buf.dispatch(self.x, self.topk, self.w, self.layout, self.cfg.use_fp8,
+                          out=(self.recv_x, self.recv_scales, self.recv_w, self.handle))
+
+    def combine_op(self):
+        self.buf.combine(self.expert_out, self.handle, self.w, out=self.y)
+
+    def kept_slots(self):
+        return int((self.handle.pos >= 0).sum().item())
+
+
+def timed(torch, ops, K, W):
+    """W untimed warmups, then exactly K steps between synchronizations; HIP
+    events (torch's current stream = the launch stream) bracket every op."""
+    for _ in range(W):
+        for op in ops:
+            op()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(ops) + 1)] for _ in range(K)]
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record()
+        for j, op in enumerate(ops):
+            op()
+            ev[i][j + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_op = [sum(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(K)) / K for j in range(len(ops))]
+    return wall / K * 1e3, per_op  # ms per step, ms per op
+
+
+def graph_timed(torch, ops, K, W, inner=20):
+    """Capture `inner` consecutive steps in one HIP graph (the launch-bound
+    decode path), replay it; returns (GPU us per step from events, wall us per
+    step). Capture follows a warmup on a side stream, as torch requires."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(W):
+            for op in ops:
+                op()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(inner):
+            for op in ops:
+                op()
+    g.replay()
+    torch.cuda.synchronize()
+    reps = max(1, K // inner)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    n = reps * inner
+    return e0.elapsed_time(e1) * 1e3 / n, wall * 1e6 / n
+
+
+def source_sha():
+    h = hashlib.sha256()
+    for f in ("ep_kernels.hip", "ep_api.hip", "ep_internal.h"):
+        with open(os.path.join(ROOT, "combine_get_dispatch_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel sources (else None)."""
+    path = os.path.join(PROFILES, "traffic.json")
+    try:
+        with open(path) as f:
+            d = json.load(f)
+        e = d[workload][kernel]
+        if e.get("source_sha") != source_sha():
+            return None
+        return e["hbm_bytes_per_launch"]
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(path, seconds):
+    """The oracle as it stands (single-threaded C) on the same workload:
+    layout + positions + FP8 dispatch + combine, repeated whole steps until
+    about `seconds` of CPU time have elapsed."""
+    import numpy as np
+    import oracle
+    cfg = path.cfg
+    wl = path.wl
+    orc = oracle.default()
+    cap = path.cap
+    n = cfg.R * cap
+    eo = path.expert_out.view(path.torch.int16).cpu().numpy().view(np.uint16)
+    steps = 0
+    t0 = time.perf_counter()
+    nk = 0
+    while True:
+        L = orc.layout(wl.topk_idx, cfg.E, cfg.R, cap)
+        pos, _ = orc.positions(wl.topk_idx, L, cfg.E, cfg.R, cap)
+        orc.dispatch(wl.x, wl.topk_w, pos, n, cfg.use_fp8)
+        orc.combine(eo, pos, wl.topk_w)
+        nk = int((pos >= 0).sum())
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or steps >= 50:
+            break
+    d, c, _ = algo_bytes(cfg.T, cfg.k, cfg.H, nk, cfg.use_fp8)
+    per_step = el / steps
+    return {"value": round((d + c) / per_step / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{steps} whole {cfg.name} steps (layout+positions+dispatch+combine, "
+                      f"T={cfg.T}), {per_step * 1e3:.1f} ms/step, single-threaded C oracle",
+            "ms_per_step": round(per_step * 1e3, 2)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (--gpus {args.gpus} requested); "
+              "the multi-GPU exchange is not part of it.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from combine_get_dispatch_amd import ep, workloads
+    ep.load()
+    torch.cuda.set_device(0)
+    cfg = workloads.CONFIGS[args.config]
+    K, W = args.steps, args.warmup
+
+    main_path = Path(cfg, args.seed, torch, ep, workloads)
+    ms, per_op = timed(torch, [main_path.layout_op, main_path.dispatch_op, main_path.combine_op], K, W)
+    st = main_path.buf.status()
+    if st:
+        raise SystemExit(f"bench: device status {st} on {cfg.name}")
+    N = main_path.kept_slots()
+    d_bytes, c_bytes, cb_bytes = algo_bytes(cfg.T, cfg.k, cfg.H, N, cfg.use_fp8)
+    value = (d_bytes + c_bytes) / (ms * 1e-3) / 1e9
+    lay_ms, dis_ms, com_ms = per_op
+    achieved = c_bytes / (com_ms * 1e-3) / 1e9
+    traffic = measured_traffic("combine", cfg.name)
+
+    out = {
+        "metric": "dispatch+combine HBM GB/s & % of peak, 4096x7168 top-8; us at 128 tokens",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8-e4m3 dispatch / bf16 rows / fp32 accumulate" if cfg.use_fp8 else "bf16 / fp32 accumulate",
+        "data": "synthetic (seeded)",
+        "config": {"workload": cfg.name, "tokens": cfg.T, "hidden": cfg.H, "experts": cfg.E,
+                   "ranks_simulated": cfg.R, "topk": cfg.k, "routing": cfg.routing,
+                   "fp8_dispatch": cfg.use_fp8, "cap_rows": main_path.cap, "kept_slots": N,
+                   "step": "layout + dispatch + combine"},
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "roofline": {"bound": "hbm", "kernel": "k_combine", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "algorithmic_bytes_per_launch": c_bytes},
+        "kernels": {
+            "layout": {"us": round(lay_ms * 1e3, 2)},
+            "dispatch": {"us": round(dis_ms * 1e3, 2), "bytes": d_bytes,
+                         "GBps": round(d_bytes / (dis_ms * 1e-3) / 1e9, 1)},
+            "combine": {"us": round(com_ms * 1e3, 2), "bytes": c_bytes,
+                        "GBps": round(achieved, 1)},
+        },
+    }
+    print(f"# main: {ms * 1e3:.1f} us/step  layout {lay_ms * 1e3:.1f}  dispatch {dis_ms * 1e3:.1f}  "
+          f"combine {com_ms * 1e3:.1f} us", file=sys.stderr, flush=True)
+
+    if not args.no_extras:
+        # backward pair on the same handle (bf16 gradients)
+        p = main_path
+        n = p.buf.num_rows
+        gy = workloads.device_normal_bf16((cfg.T, cfg.H), seed=args.seed + 202)
+        grows = torch.empty((n, cfg.H), dtype=torch.bfloat16, device="cuda")
+        gx = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device="cuda")
+        bms, (cb_ms, db_ms) = timed(torch, [lambda: p.buf.combine_backward(gy, p.handle, out=grows),
+                                            lambda: p.buf.dispatch_backward(p.expert_out, p.handle, p.w, out=gx)],
+                                    K, W)
+        out["backward"] = {"workload": cfg.name, "us_per_step": round(bms * 1e3, 2),
+                           "combine_backward": {"us": round(cb_ms * 1e3, 2),
+                                                "GBps": round(cb_bytes / (cb_ms * 1e-3) / 1e9, 1)},
+                           "dispatch_backward": {"us": round(db_ms * 1e3, 2),
+                                                 "GBps": round(c_bytes / (db_ms * 1e-3) / 1e9, 1)},
+                           "GBps": round((cb_bytes + c_bytes) / (bms * 1e-3) / 1e9, 1)}
+        del grows, gx, gy
+        # plain streaming copy of the combine's byte count (attainable bandwidth)
+        nb = (c_bytes // 2) // 16 * 16
+        src = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        dst = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        src.fill_(1)
+        cms, (copy_ms,) = timed(torch, [lambda: ep.copy_bytes(src, dst)], K, W)
+        out["copy_reference"] = {"bytes_moved": 2 * nb, "us": round(copy_ms * 1e3, 2),
+                                 "GBps": round(2 * nb / (copy_ms * 1e-3) / 1e9, 1)}
+        del src, dst
+        # decode latency: 128 tokens (one rank's share) and the 8-rank group.
+        # The step is launch-bound, so it is captured in a HIP graph and
+        # replayed; eager per-op event times (host launch gaps included) are
+        # reported beside it.
+        dec = {}
+        for name in ("decode_rank", "decode"):
+            dp = Path(workloads.CONFIGS[name], args.seed, torch, ep, workloads)
+            ops = [dp.layout_op, dp.dispatch_op, dp.combine_op]
+            g_us, g_wall = graph_timed(torch, ops, max(K, 200), W)
+            dms, (l_, d_, c_) = timed(torch, ops, max(K, 100), W)
+            dst_ = dp.buf.status()
+            dd, dc, _ = algo_bytes(dp.cfg.T, dp.cfg.k, dp.cfg.H, dp.kept_slots(), True)
+            dec[name] = {"tokens": dp.cfg.T, "us_per_step_graph": round(g_us, 2),
+                         "us_per_step_graph_wall": round(g_wall, 2),
+                         "GBps_graph": round((dd + dc) / (g_us * 1e-6) / 1e9, 1),
+                         "us_per_step_eager": round(dms * 1e3, 2),
+                         "eager_layout_us": round(l_ * 1e3, 2), "eager_dispatch_us": round(d_ * 1e3, 2),
+                         "eager_combine_us": round(c_ * 1e3, 2), "status": dst_}
+            dp.buf.close()
+            del dp
+        out["decode"] = dec
+        out["us_at_128_tokens"] = dec["decode_rank"]["us_per_step_graph"]
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(main_path, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,368 @@
+// ep_api.hip -- host side of the C ABI declared in include/ep.h: argument
+// validation, the per-context workspace, launch geometry and status words.
+// Every step of the hot path runs in the kernels of ep_kernels.hip.
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+
+#include "ep.h"
+#include "ep_internal.h"
+
+struct ep_ctx {
+    ep_config cfg;
+    int device;
+    int num_tiles;
+    int keys;  // E + R
+    void *ws;
+    size_t ws_bytes;
+    uint32_t *counters;
+    uint64_t *tile_state;
+    int32_t *bp;
+    uint32_t *bp_ready;
+    uint32_t spin_limit;
+    bool debug;
+};
+
+namespace {
+
+// Waves a token-major launch aims for. Dispatch (write-heavy, one read of x
+// per token) keeps a token's passes in one wave; combine (k gathered rows per
+// pass) splits every token into one wave per 1024-channel pass, which keeps
+// more independent row loads in flight.
+constexpr int kDispatchTargetWaves = 2048;  // ~8 waves per CU on 256 CUs
+constexpr int kCombineTargetWaves = 1 << 30;  // i.e. one pass per wave
+constexpr int kMaxPassPerWave = 8;   // must match ep_kernels.hip
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int validate_config(const ep_config *c) {
+    if (!c) return EP_ERR_ARG;
+    if (c->reserved != 0) return EP_ERR_ARG;
+    if (c->num_ranks < 1 || c->num_ranks > ep::kMaxRanks) return EP_ERR_ARG;
+    if (c->num_tokens < 0 || c->num_tokens > (1 << 24) || c->num_tokens % c->num_ranks) return EP_ERR_ARG;
+    if (c->num_topk < 1 || c->num_topk > ep::kMaxTopk) return EP_ERR_ARG;
+    if (c->num_experts < 1 || c->num_experts > ep::kMaxExperts || c->num_experts % c->num_ranks)
+        return EP_ERR_ARG;
+    if (c->hidden < 8 || c->hidden > 65536 || c->hidden % 8) return EP_ERR_ARG;
+    if (c->cap_rows < 0 || (int64_t)c->num_ranks * c->cap_rows >= ((int64_t)1 << 31)) return EP_ERR_ARG;
+    return EP_OK;
+}
+
+int num_tiles_of(const ep_config &c) {
+    const int n = (c.num_tokens + ep::kLayoutTile - 1) / ep::kLayoutTile;
+    return n > 0 ? n : 1;
+}
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// workspace: counters | tile states | boundary prefixes | boundary-ready flags
+size_t workspace_layout(const ep_config &c, size_t *off_state, size_t *off_bp, size_t *off_ready) {
+    const size_t keys = (size_t)c.num_experts + c.num_ranks;
+    size_t off = round_up(ep::kNumCounters * sizeof(uint32_t), 256);
+    *off_state = off;
+    off = round_up(off + (size_t)num_tiles_of(c) * keys * sizeof(uint64_t), 256);
+    *off_bp = off;
+    off = round_up(off + ((size_t)c.num_ranks + 1) * keys * sizeof(int32_t), 256);
+    *off_ready = off;
+    off = round_up(off + (size_t)num_tiles_of(c) * sizeof(uint32_t), 256);
+    return off;
+}
+
+// Work split of a token-major kernel: waves_per_token waves share a token's
+// rows, each taking passes_per_wave passes of 1024 channels.
+struct Geometry {
+    int npass, wpt, ppw, num_waves;
+};
+
+Geometry geometry(int T, int H, int target_waves) {
+    Geometry g;
+    g.npass = (H + 1023) / 1024;
+    int w = T > 0 ? (int)(((int64_t)target_waves + T - 1) / T) : 1;
+    const int minw = (g.npass + kMaxPassPerWave - 1) / kMaxPassPerWave;
+    if (w < minw) w = minw;
+    if (w > g.npass) w = g.npass;
+    g.ppw = (g.npass + w - 1) / w;
+    g.wpt = (g.npass + g.ppw - 1) / g.ppw;
+    g.num_waves = T * g.wpt;
+    return g;
+}
+
+int hip_fail(hipError_t e, const char *what) {
+    if (e == hipSuccess) return EP_OK;
+    std::fprintf(stderr, "libep: %s failed: %s\n", what, hipGetErrorString(e));
+    return EP_ERR_HIP;
+}
+
+int check_handle(const ep_ctx *ctx, const ep_handle *h) {
+    if (!h) return EP_ERR_ARG;
+    if (h->num_tokens != ctx->cfg.num_tokens || h->num_topk != ctx->cfg.num_topk) return EP_ERR_ARG;
+    if (!h->pos && ctx->cfg.num_tokens > 0) return EP_ERR_ARG;
+    return EP_OK;
+}
+
+int combine_common(ep_ctx *ctx, const uint16_t *rows, const ep_handle *h, const float *w, void *out,
+                   bool out_f32, ep_stream_t stream, const char *name) {
+    if (!ctx) return EP_ERR_ARG;
+    if (int r = check_handle(ctx, h)) return r;
+    const ep_config &c = ctx->cfg;
+    if (c.num_tokens == 0) return EP_OK;
+    if (!out || (!rows && c.cap_rows > 0)) return EP_ERR_ARG;
+    if (!aligned(out, 16) || !aligned(rows, 16) || !aligned(h->pos, 4) || !aligned(w, 4)) return EP_ERR_ALIGN;
+    const Geometry g = geometry(c.num_tokens, c.hidden, kCombineTargetWaves);
+    ep::CombineArgs a;
+    a.rows = rows;
+    a.pos = h->pos;
+    a.w = w;
+    a.out = out;
+    a.T = c.num_tokens;
+    a.k = c.num_topk;
+    a.H = c.hidden;
+    a.num_rows = (int64_t)c.num_ranks * c.cap_rows;
+    a.waves_per_token = g.wpt;
+    a.passes_per_wave = g.ppw;
+    a.npass = g.npass;
+    a.counters = ctx->counters;
+    if (ctx->debug)
+        std::fprintf(stderr, "libep: %s T=%d k=%d H=%d waves=%d (%d/token, %d passes each)\n", name, a.T, a.k,
+                     a.H, g.num_waves, g.wpt, g.ppw);
+    return hip_fail(ep::launch_combine(a, out_f32, g.num_waves, (hipStream_t)stream), name);
+}
+
+int dispatch_common(ep_ctx *ctx, const uint16_t *x, const int32_t *topk, const float *w, const ep_layout *L,
+                    bool fp8, bool forward, void *recv_x, float *recv_scales, float *recv_w, ep_handle *h,
+                    ep_stream_t stream, const char *name) {
+    const ep_config &c = ctx->cfg;
+    if (c.num_tokens == 0) return EP_OK;
+    if (!x || (!recv_x && c.cap_rows > 0)) return EP_ERR_ARG;
+    if (!aligned(x, 16) || !aligned(recv_x, 16) || !aligned(h->pos, 4)) return EP_ERR_ALIGN;
+    const Geometry g = geometry(c.num_tokens, c.hidden, kDispatchTargetWaves);
+    ep::DispatchArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.x = x;
+    a.topk = topk;
+    a.w = w;
+    a.pos = h->pos;
+    a.src_idx = h->src_idx;
+    a.recv_w = (w && recv_w) ? recv_w : nullptr;
+    a.recv_x = recv_x;
+    a.recv_scales = recv_scales;
+    if (forward) {
+        a.rank_in_expert = L->rank_in_expert;
+        a.expert_off = L->expert_off;
+    }
+    a.T = c.num_tokens;
+    a.k = c.num_topk;
+    a.E = c.num_experts;
+    a.epr = c.num_experts / c.num_ranks;
+    a.H = c.hidden;
+    a.cap_rows = c.cap_rows;
+    a.num_rows = (int64_t)c.num_ranks * c.cap_rows;
+    a.waves_per_token = g.wpt;
+    a.passes_per_wave = g.ppw;
+    a.npass = g.npass;
+    a.counters = ctx->counters;
+    if (ctx->debug)
+        std::fprintf(stderr, "libep: %s T=%d k=%d H=%d fp8=%d waves=%d (%d/token, %d passes each)\n", name,
+                     a.T, a.k, a.H, (int)fp8, g.num_waves, g.wpt, g.ppw);
+    return hip_fail(ep::launch_dispatch(a, fp8, forward, g.num_waves, (hipStream_t)stream), name);
+}
+
+}  // namespace
+
+extern "C" {
+
+int ep_version(void) { return EP_ABI_VERSION; }
+
+const char *ep_strerror(int code) {
+    switch (code) {
+        case EP_OK: return "ok";
+        case EP_ERR_ARG: return "invalid argument";
+        case EP_ERR_ALIGN: return "misaligned pointer (row arrays need 16-byte alignment)";
+        case EP_ERR_HIP: return "HIP runtime error";
+        case EP_ERR_NOMEM: return "out of device memory";
+        default: return "unknown error";
+    }
+}
+
+int ep_query_sizes(const ep_config *cfg, ep_sizes *out) {
+    if (int r = validate_config(cfg)) return r;
+    if (!out) return EP_OK;
+    const size_t T = cfg->num_tokens, k = cfg->num_topk, E = cfg->num_experts, R = cfg->num_ranks,
+                 H = cfg->hidden, rows = R * (size_t)cfg->cap_rows;
+    out->cnt_se = R * E * 4;
+    out->cnt_sd = R * R * 4;
+    out->recv_cnt = E * 4;
+    out->expert_off = E * 4;
+    out->rank_rows = R * 4;
+    out->src_expert_off = R * E * 4;
+    out->rank_in_expert = T * k * 4;
+    out->is_token_in_rank = T * R;
+    out->pos = T * k * 4;
+    out->src_idx = rows * 4;
+    out->x = T * H * 2;
+    out->recv_x_bf16 = rows * H * 2;
+    out->recv_x_fp8 = rows * H;
+    out->recv_scales = rows * (H / 128) * 4;
+    out->recv_w = rows * 4;
+    out->combined_x = T * H * 2;
+    size_t a, b, r;
+    out->workspace = workspace_layout(*cfg, &a, &b, &r);
+    return EP_OK;
+}
+
+int ep_create(const ep_config *cfg, ep_ctx **out) {
+    if (!out) return EP_ERR_ARG;
+    *out = nullptr;
+    if (int r = validate_config(cfg)) return r;
+    ep_ctx *ctx = new (std::nothrow) ep_ctx();
+    if (!ctx) return EP_ERR_NOMEM;
+    ctx->cfg = *cfg;
+    ctx->num_tiles = num_tiles_of(*cfg);
+    ctx->keys = cfg->num_experts + cfg->num_ranks;
+    size_t off_state, off_bp, off_ready;
+    ctx->ws_bytes = workspace_layout(*cfg, &off_state, &off_bp, &off_ready);
+    const char *dbg = std::getenv("EP_DEBUG");
+    ctx->debug = dbg && dbg[0] && dbg[0] != '0';
+    const char *spin = std::getenv("EP_SPIN_LIMIT");
+    ctx->spin_limit = spin ? (uint32_t)std::strtoul(spin, nullptr, 10) : (1u << 20);
+    if (hipGetDevice(&ctx->device) != hipSuccess) {
+        delete ctx;
+        return EP_ERR_HIP;
+    }
+    if (hipMalloc(&ctx->ws, ctx->ws_bytes) != hipSuccess) {
+        delete ctx;
+        return EP_ERR_NOMEM;
+    }
+    char *base = static_cast<char *>(ctx->ws);
+    ctx->counters = reinterpret_cast<uint32_t *>(base);
+    ctx->tile_state = reinterpret_cast<uint64_t *>(base + off_state);
+    ctx->bp = reinterpret_cast<int32_t *>(base + off_bp);
+    ctx->bp_ready = reinterpret_cast<uint32_t *>(base + off_ready);
+    uint32_t init[ep::kNumCounters] = {0};
+    init[ep::kEpoch] = 1;  // tile states start at epoch 0 = "not published"
+    int r = hip_fail(hipMemset(ctx->ws, 0, ctx->ws_bytes), "hipMemset");
+    if (!r) r = hip_fail(hipMemcpy(ctx->counters, init, sizeof init, hipMemcpyHostToDevice), "hipMemcpy");
+    if (!r) r = hip_fail(hipDeviceSynchronize(), "hipDeviceSynchronize");
+    if (r) {
+        (void)hipFree(ctx->ws);
+        delete ctx;
+        return r;
+    }
+    if (ctx->debug)
+        std::fprintf(stderr, "libep: ctx T=%d k=%d E=%d R=%d H=%d cap_rows=%lld tiles=%d workspace=%zu B\n",
+                     cfg->num_tokens, cfg->num_topk, cfg->num_experts, cfg->num_ranks, cfg->hidden,
+                     (long long)cfg->cap_rows, ctx->num_tiles, ctx->ws_bytes);
+    *out = ctx;
+    return EP_OK;
+}
+
+int ep_destroy(ep_ctx *ctx) {
+    if (!ctx) return EP_OK;
+    int r = hip_fail(hipDeviceSynchronize(), "hipDeviceSynchronize");
+    if (hipFree(ctx->ws) != hipSuccess && !r) r = EP_ERR_HIP;
+    delete ctx;
+    return r;
+}
+
+int ep_get_dispatch_layout(ep_ctx *ctx, const int32_t *topk_idx, const ep_layout *L, ep_stream_t stream) {
+    if (!ctx || !L) return EP_ERR_ARG;
+    const ep_config &c = ctx->cfg;
+    if (!L->cnt_se || !L->cnt_sd || !L->recv_cnt || !L->expert_off || !L->rank_rows || !L->src_expert_off)
+        return EP_ERR_ARG;
+    if (c.num_tokens > 0 && (!topk_idx || !L->rank_in_expert || !L->is_token_in_rank)) return EP_ERR_ARG;
+    if (!aligned(topk_idx, 4) || !aligned(L->rank_in_expert, 16) || !aligned(L->is_token_in_rank, 16) ||
+        !aligned(L->cnt_se, 4) || !aligned(L->cnt_sd, 4) || !aligned(L->recv_cnt, 4) ||
+        !aligned(L->expert_off, 4) || !aligned(L->rank_rows, 4) || !aligned(L->src_expert_off, 4))
+        return EP_ERR_ALIGN;
+    ep::LayoutArgs a;
+    a.topk = topk_idx;
+    a.T = c.num_tokens;
+    a.k = c.num_topk;
+    a.E = c.num_experts;
+    a.R = c.num_ranks;
+    a.epr = c.num_experts / c.num_ranks;
+    a.tpr = c.num_tokens / c.num_ranks;
+    a.num_tiles = ctx->num_tiles;
+    a.use_ticket = ctx->num_tiles > ep::kCoResidentTiles;
+    a.cap_rows = c.cap_rows;
+    a.rank_in_expert = L->rank_in_expert;
+    a.itr = L->is_token_in_rank;
+    a.cnt_se = L->cnt_se;
+    a.cnt_sd = L->cnt_sd;
+    a.recv_cnt = L->recv_cnt;
+    a.expert_off = L->expert_off;
+    a.rank_rows = L->rank_rows;
+    a.src_expert_off = L->src_expert_off;
+    a.tile_state = ctx->tile_state;
+    a.bp = ctx->bp;
+    a.bp_ready = ctx->bp_ready;
+    a.counters = ctx->counters;
+    a.spin_limit = ctx->spin_limit;
+    if (ctx->debug)
+        std::fprintf(stderr, "libep: layout T=%d k=%d E=%d R=%d tiles=%d\n", a.T, a.k, a.E, a.R, a.num_tiles);
+    return hip_fail(ep::launch_layout(a, (hipStream_t)stream), "ep_get_dispatch_layout");
+}
+
+int ep_dispatch(ep_ctx *ctx, const uint16_t *x, const int32_t *topk_idx, const float *topk_weights,
+                const ep_layout *L, int use_fp8, void *recv_x, float *recv_scales, float *recv_w,
+                ep_handle *handle, ep_stream_t stream) {
+    if (!ctx || !L || !handle) return EP_ERR_ARG;
+    const ep_config &c = ctx->cfg;
+    if (use_fp8 != 0 && use_fp8 != 1) return EP_ERR_ARG;
+    if (use_fp8 && (c.hidden % 128 || (!recv_scales && c.cap_rows > 0))) return EP_ERR_ARG;
+    if (!use_fp8 && recv_scales) return EP_ERR_ARG;
+    if ((!handle->pos && c.num_tokens > 0) || (!handle->src_idx && c.cap_rows > 0)) return EP_ERR_ARG;
+    if (c.num_tokens > 0 && (!topk_idx || !L->rank_in_expert || !L->expert_off)) return EP_ERR_ARG;
+    if (!aligned(topk_idx, 4) || !aligned(topk_weights, 4) || !aligned(recv_w, 4) || !aligned(recv_scales, 4) ||
+        !aligned(handle->src_idx, 4))
+        return EP_ERR_ALIGN;
+    handle->num_tokens = c.num_tokens;
+    handle->num_topk = c.num_topk;
+    return dispatch_common(ctx, x, topk_idx, topk_weights, L, use_fp8 != 0, true, recv_x, recv_scales, recv_w,
+                           handle, stream, "ep_dispatch");
+}
+
+int ep_combine(ep_ctx *ctx, const uint16_t *expert_out, const ep_handle *handle, const float *weights,
+               uint16_t *combined_x, ep_stream_t stream) {
+    return combine_common(ctx, expert_out, handle, weights, combined_x, false, stream, "ep_combine");
+}
+
+int ep_combine_f32(ep_ctx *ctx, const uint16_t *expert_out, const ep_handle *handle, const float *weights,
+                   float *combined_f32, ep_stream_t stream) {
+    return combine_common(ctx, expert_out, handle, weights, combined_f32, true, stream, "ep_combine_f32");
+}
+
+int ep_combine_backward(ep_ctx *ctx, const uint16_t *grad_combined, const ep_handle *handle,
+                        uint16_t *grad_rows, ep_stream_t stream) {
+    if (!ctx) return EP_ERR_ARG;
+    if (int r = check_handle(ctx, handle)) return r;
+    ep_handle h = *handle;
+    return dispatch_common(ctx, grad_combined, nullptr, nullptr, nullptr, false, false, grad_rows, nullptr,
+                           nullptr, &h, stream, "ep_combine_backward");
+}
+
+int ep_dispatch_backward(ep_ctx *ctx, const uint16_t *grad_rows, const ep_handle *handle, const float *weights,
+                         uint16_t *grad_x, ep_stream_t stream) {
+    return combine_common(ctx, grad_rows, handle, weights, grad_x, false, stream, "ep_dispatch_backward");
+}
+
+int ep_get_status(ep_ctx *ctx, ep_stream_t stream, uint32_t *status) {
+    if (!ctx || !status) return EP_ERR_ARG;
+    int r = hip_fail(hipStreamSynchronize((hipStream_t)stream), "hipStreamSynchronize");
+    if (r) return r;
+    r = hip_fail(hipMemcpy(status, ctx->counters + ep::kStatus, sizeof(uint32_t), hipMemcpyDeviceToHost),
+                 "hipMemcpy");
+    if (r) return r;
+    const uint32_t zero = 0;
+    return hip_fail(hipMemcpy(ctx->counters + ep::kStatus, &zero, sizeof zero, hipMemcpyHostToDevice), "hipMemcpy");
+}
+
+int ep_copy_bytes(const void *src, void *dst, size_t bytes, ep_stream_t stream) {
+    if (bytes == 0) return EP_OK;
+    if (!src || !dst || bytes % 16) return EP_ERR_ARG;
+    if (!aligned(src, 16) || !aligned(dst, 16)) return EP_ERR_ALIGN;
+    return hip_fail(ep::launch_copy(src, dst, bytes / 16, (hipStream_t)stream), "ep_copy_bytes");
+}
+
+}  // extern "C"

@@ -1,0 +1,73 @@
+// ep_internal.h -- kernel launch interface shared by ep_api.hip and ep_kernels.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ep {
+
+// Layout scan geometry: one workgroup of 256 threads (4 waves) handles 256
+// consecutive tokens, one token per lane; a single tile skips the cross-tile
+// machinery. LDS per key: 4 wave masks (8 B), 4 wave prefixes, the tile's
+// exclusive prefix and count (4 B each).
+constexpr int kLayoutTile = 256;
+constexpr int kCoResidentTiles = 256;  // grids up to this size number tiles by block index
+inline size_t layout_lds_bytes(int keys) { return (size_t)keys * (4 * 8 + 4 * 4 + 2 * 4); }
+constexpr int kMaxTopk = 32;
+constexpr int kMaxRanks = 64;
+constexpr int kMaxExperts = 1024;
+
+// ctx workspace counters (uint32 each)
+enum Counter { kTicket = 0, kDone = 1, kEpoch = 2, kStatus = 3, kNumCounters = 16 };
+
+struct LayoutArgs {
+    const int32_t *topk;
+    int T, k, E, R, epr, tpr, num_tiles;
+    int use_ticket;  // number tiles by start order (large grids) instead of block index
+    int64_t cap_rows;
+    int32_t *rank_in_expert;
+    uint8_t *itr;
+    int32_t *cnt_se, *cnt_sd, *recv_cnt, *expert_off, *rank_rows, *src_expert_off;
+    uint64_t *tile_state;  // [num_tiles][E+R]
+    int32_t *bp;           // [R+1][E+R] prefixes at source-rank boundaries
+    uint32_t *bp_ready;    // [num_tiles] epoch once a tile's boundary prefixes are written
+    uint32_t *counters;
+    uint32_t spin_limit;
+};
+
+struct DispatchArgs {
+    const uint16_t *x;           // [T][H] bf16 (or grad_combined for combine_backward)
+    const int32_t *topk;         // [T][k]        (forward only)
+    const float *w;              // [T][k] or NULL (forward only)
+    const int32_t *rank_in_expert;  // [T][k]     (forward only)
+    const int32_t *expert_off;   // [E]           (forward only)
+    int32_t *pos;                // [T][k] written (forward) or read (backward)
+    int32_t *src_idx;            // [R*cap] (forward only)
+    float *recv_w;               // [R*cap] or NULL (forward only)
+    void *recv_x;                // [R*cap][H] e4m3 or bf16
+    float *recv_scales;          // [R*cap][H/128] (FP8 only)
+    int T, k, E, epr, H;
+    int64_t cap_rows, num_rows;  // num_rows = R * cap_rows
+    int waves_per_token, passes_per_wave, npass;
+    uint32_t *counters;
+};
+
+struct CombineArgs {
+    const uint16_t *rows;  // [R*cap][H] bf16
+    const int32_t *pos;    // [T][k]
+    const float *w;        // [T][k] or NULL
+    void *out;             // [T][H] bf16 or fp32
+    int T, k, H;
+    int64_t num_rows;      // rows of `rows`; positions outside are skipped
+    int waves_per_token, passes_per_wave, npass;
+    uint32_t *counters;
+};
+
+hipError_t launch_layout(const LayoutArgs &a, hipStream_t s);
+hipError_t launch_dispatch(const DispatchArgs &a, bool fp8, bool forward, int num_waves,
+                           hipStream_t s);
+hipError_t launch_combine(const CombineArgs &a, bool out_f32, int num_waves, hipStream_t s);
+hipError_t launch_copy(const void *src, void *dst, size_t n16, hipStream_t s);
+
+}  // namespace ep

@@ -1,0 +1,722 @@
+// ep_kernels.hip -- gfx950 kernels of the MoE dispatch / combine hot path.
+//
+//   k_layout    dispatch layout: per-wave expert bitmasks in LDS (ds_or_b64)
+//               and per-rank bitmasks from wave ballots, popcount ranks, and a
+//               single-pass decoupled look-back scan (Merrill & Garland,
+//               "Single-pass Parallel Prefix Scan with Decoupled Look-back",
+//               2016) over per-tile expert/rank counts; each tile writes the
+//               per-source outputs at the boundaries it owns and the last
+//               tile the totals and offsets.
+//   k_dispatch  token-major pack: each wave reads a token's row once with
+//               128-bit non-temporal loads and writes it to the token's k
+//               receive rows with 128-bit stores; in FP8 mode the per-128-channel amax is reduced
+//               across 8 lanes with DPP and the row is packed with
+//               v_cvt_pk_fp8_f32 (OCP e4m3 on gfx950).
+//   k_combine   token-major gather-reduce: each wave loads the token's k rows
+//               (all slots in flight) and accumulates in fp32 with one fused
+//               multiply-add per slot in slot order, then rounds to bf16.
+//   k_copy      plain 128-bit streaming copy (bandwidth calibration).
+//
+// The operations follow the DeepEP usage guide's dispatch / combine /
+// backward interface (zhouruolin.cn DeepEP guide, section 5); the arithmetic
+// each kernel implements is stated in include/ep.h.
+#include "ep_internal.h"
+
+namespace ep {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr uint32_t kStBad = 1u, kStDup = 2u, kStCap = 4u, kStTimeout = 8u, kStBadHandle = 16u;
+constexpr int kWavesPerBlock = 4;
+constexpr int kMaxPassPerWave = 8;  // dispatch: 1024 channels per pass
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+// fp32 -> bf16, round to nearest even (bias 0x7fff plus the kept lsb); NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// max with the value DPP control CTRL routes into this lane
+template <int CTRL>
+__device__ __forceinline__ float dpp_max(float v) {
+    return fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false)));
+}
+
+__device__ __forceinline__ int readlane_i(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
+__device__ __forceinline__ float readlane_f(float v, int lane) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// ---------------------------------------------------------------------------
+// layout
+// ---------------------------------------------------------------------------
+
+// Look-back tile state: [63:34] epoch, [33:32] flag, [31:0] count. A word
+// whose epoch differs from the current call's is "not yet published", so the
+// states never need clearing between calls.
+constexpr uint64_t kFlagAgg = 1, kFlagPrefix = 2;
+
+__device__ __forceinline__ uint64_t pack_state(uint32_t epoch, uint64_t flag, uint32_t v) {
+    return ((uint64_t)epoch << 34) | (flag << 32) | (uint64_t)v;
+}
+
+constexpr int kLookbackWindow = 16;  // predecessor states read per round trip
+constexpr int kTileWaves = 4;
+constexpr int kTileTokens = kTileWaves * 64;
+
+// Exclusive prefix sum of one int per thread over the block (wave scan with
+// lane shuffles, then the wave totals). *total receives the block sum.
+__device__ __forceinline__ int block_exclusive_scan(int v, int *s_part, int *total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(x, d, 64);
+        if (lane >= d) x += y;
+    }
+    if (lane == 63) s_part[wave] = x;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int run = 0;
+        for (int w = 0; w < kTileWaves; ++w) {
+            const int c = s_part[w];
+            s_part[w] = run;
+            run += c;
+        }
+        s_part[kTileWaves] = run;
+    }
+    __syncthreads();
+    *total = s_part[kTileWaves];
+    return s_part[wave] + x - v;
+}
+
+// Tokens of this tile before tile-local position nb that hold `key`
+// (wpre[w][key] = such tokens in waves before w).
+__device__ __forceinline__ int count_before(const uint64_t *masks, const int32_t *wpre, int K, int key, int nb,
+                                            int ntile) {
+    if (nb <= 0) return 0;
+    if (nb > ntile) nb = ntile;
+    const int w = nb >> 6, l = nb & 63;
+    if (w == kTileWaves) return wpre[(w - 1) * K + key] + __popcll(masks[(w - 1) * K + key]);
+    const int c = wpre[w * K + key];
+    return l ? c + __popcll(masks[w * K + key] & ((1ull << l) - 1)) : c;
+}
+
+// Tile owning source-rank boundary b (token index; b == T is the end).
+__device__ __forceinline__ int boundary_owner(int b, int T, int num_tiles) {
+    return b < T ? b / kTileTokens : num_tiles - 1;
+}
+
+template <int KMAX>
+__global__ __launch_bounds__(kTileTokens) void k_layout(LayoutArgs a) {
+    extern __shared__ uint64_t lds[];
+    const int K = a.E + a.R;                   // keys: experts, then ranks
+    uint64_t *masks = lds;                     // [4 waves][K] token bitmasks per wave
+    int32_t *wpre = reinterpret_cast<int32_t *>(masks + kTileWaves * K);  // [4][K] tokens in earlier waves
+    int32_t *excl = wpre + kTileWaves * K;     // [K] tokens in earlier tiles
+    int32_t *agg = excl + K;                   // [K] tokens in this tile
+    int32_t *scan = wpre;                      // last step only: [E+1] prefix of expert rows
+    __shared__ int s_tile, s_part[kTileWaves + 1];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const bool single = a.num_tiles == 1;
+    uint32_t epoch = 0;
+    if (!single) epoch = __hip_atomic_load(&a.counters[kEpoch], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+    // A tile only waits on lower-numbered tiles. Small grids are co-resident,
+    // so the block index is the tile; larger grids number tiles in the order
+    // they start (a ticket), so every predecessor is already running.
+    if (tid == 0) s_tile = a.use_ticket ? (int)atomicAdd(&a.counters[kTicket], 1u) : (int)blockIdx.x;
+    for (int i = tid; i < kTileWaves * K; i += kTileTokens) masks[i] = 0;
+    __syncthreads();
+    const int tile = s_tile;
+    if (tile >= a.num_tiles) {  // workspace not re-armed (an earlier call did not finish)
+        if (tid == 0) atomicOr(&a.counters[kStatus], kStTimeout);
+        return;
+    }
+    const int t0 = tile * kTileTokens;
+    const int t = t0 + tid;
+    const int ntile = max(min(kTileTokens, a.T - t0), 0);  // tokens in this tile
+    const bool last_tile = tile == a.num_tiles - 1;
+    const uint64_t bit = 1ull << lane;
+
+    // 1. validate the token's slots; expert bits go into the wave's masks
+    //    (LDS atomics), the per-rank bits are wave ballots (no atomics: every
+    //    lane would hit the same few words)
+    int ev[KMAX];
+    uint32_t st = 0;
+    uint64_t rmask = 0;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) ev[j] = -1;
+    if (t < a.T) {
+        const int32_t *row = a.topk + (size_t)t * a.k;
+        int raw[KMAX];
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) raw[j] = j < a.k ? row[j] : -1;
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) {
+            const int v = raw[j];
+            if (v == -1) continue;
+            if (v < -1 || v >= a.E) {
+                st |= kStBad;
+                continue;
+            }
+            bool dup = false;
+#pragma unroll
+            for (int jj = 0; jj < j; ++jj) dup |= (ev[jj] == v);
+            if (dup) {
+                st |= kStDup;
+                continue;
+            }
+            ev[j] = v;
+            atomicOr(reinterpret_cast<unsigned long long *>(&masks[wave * K + v]), (unsigned long long)bit);
+            rmask |= 1ull << (v / a.epr);
+        }
+    }
+    {
+        uint64_t mine = 0;
+        for (int d = 0; d < a.R; ++d) {
+            const uint64_t b = __ballot((rmask >> d) & 1);
+            if (lane == d) mine = b;
+        }
+        if (lane < a.R) masks[wave * K + a.E + lane] = mine;
+    }
+    if (t < a.T) {
+        // is_token_in_rank row: R bytes, written with the widest aligned stores
+        uint8_t *out = a.itr + (size_t)t * a.R;
+        auto bytes4 = [&](int d) -> uint32_t {
+            const uint32_t x = (uint32_t)(rmask >> d) & 0xFu;
+            return (x & 1u) | ((x & 2u) << 7) | ((x & 4u) << 14) | ((x & 8u) << 21);
+        };
+        if ((a.R & 15) == 0) {
+            for (int d = 0; d < a.R; d += 16) {
+                const u32x4 v4 = {bytes4(d), bytes4(d + 4), bytes4(d + 8), bytes4(d + 12)};
+                *reinterpret_cast<u32x4 *>(out + d) = v4;
+            }
+        } else if ((a.R & 7) == 0) {
+            for (int d = 0; d < a.R; d += 8)
+                *reinterpret_cast<uint64_t *>(out + d) = (uint64_t)bytes4(d) | ((uint64_t)bytes4(d + 4) << 32);
+        } else if ((a.R & 3) == 0) {
+            for (int d = 0; d < a.R; d += 4) *reinterpret_cast<uint32_t *>(out + d) = bytes4(d);
+        } else {
+            for (int d = 0; d < a.R; ++d) out[d] = (uint8_t)((rmask >> d) & 1);
+        }
+    }
+    if (st) atomicOr(&a.counters[kStatus], st);
+    __syncthreads();
+
+    // 2. per key: tokens in earlier waves and the tile's count; published at
+    //    once for the look-back (tile 0's count is already its inclusive prefix)
+    for (int key = tid; key < K; key += kTileTokens) {
+        int c = 0;
+#pragma unroll
+        for (int w = 0; w < kTileWaves; ++w) {
+            wpre[w * K + key] = c;
+            c += __popcll(masks[w * K + key]);
+        }
+        agg[key] = c;
+        if (!single)
+            __hip_atomic_store(a.tile_state + (size_t)tile * K + key,
+                               pack_state(epoch, tile == 0 ? kFlagPrefix : kFlagAgg, (uint32_t)c),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+
+    // 3. decoupled look-back, a window of predecessors per round trip: add
+    //    counts from the nearest predecessor back to the first inclusive
+    //    prefix; a predecessor that has not published yet ends the window and
+    //    is read again. Then this tile's share of the per-source outputs:
+    //    prefixes at the source-rank boundaries it owns (boundary s = token
+    //    s*T/R): src_expert_off directly, and a copy for later tiles.
+    for (int key = tid; key < K; key += kTileTokens) {
+        int sum = 0;
+        if (tile > 0) {
+            int hi = tile - 1;
+            uint32_t spins = 0;
+            while (hi >= 0) {
+                uint64_t sv[kLookbackWindow];
+#pragma unroll
+                for (int i = 0; i < kLookbackWindow; ++i)
+                    sv[i] = (hi - i >= 0) ? __hip_atomic_load(a.tile_state + (size_t)(hi - i) * K + key,
+                                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                          : 0ull;
+                int consumed = 0;
+                bool found = false, stall = false;
+#pragma unroll
+                for (int i = 0; i < kLookbackWindow; ++i) {
+                    if (found || stall || hi - i < 0) continue;
+                    const uint32_t fl = (uint32_t)(sv[i] >> 32) & 3u;
+                    if ((uint32_t)(sv[i] >> 34) != epoch || fl == 0) {
+                        stall = true;
+                        continue;
+                    }
+                    sum += (int32_t)(uint32_t)sv[i];
+                    ++consumed;
+                    if (fl == kFlagPrefix) found = true;
+                }
+                if (found) break;
+                hi -= consumed;
+                if (stall) {
+                    if (++spins > a.spin_limit) {
+                        atomicOr(&a.counters[kStatus], kStTimeout);
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(1);
+                }
+            }
+            __hip_atomic_store(a.tile_state + (size_t)tile * K + key,
+                               pack_state(epoch, kFlagPrefix, (uint32_t)(sum + agg[key])), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
+        excl[key] = sum;
+        const bool is_expert = key < a.E;
+        if (single) {
+            // every boundary is here: per-source counts and offsets at once
+            int prev = 0;
+            for (int s = 0; s < a.R; ++s) {
+                const int nxt = count_before(masks, wpre, K, key, (s + 1) * a.tpr, ntile);
+                if (is_expert) {
+                    a.cnt_se[(size_t)s * a.E + key] = nxt - prev;
+                    a.src_expert_off[(size_t)s * a.E + key] = prev;
+                } else {
+                    a.cnt_sd[(size_t)s * a.R + (key - a.E)] = nxt - prev;
+                }
+                prev = nxt;
+            }
+        } else {
+            for (int s = 0; s <= a.R; ++s) {
+                const int b = s * a.tpr;
+                if (boundary_owner(b, a.T, a.num_tiles) != tile) continue;
+                const int pre = sum + count_before(masks, wpre, K, key, b - t0, ntile);
+                a.bp[(size_t)s * K + key] = pre;
+                if (is_expert && s < a.R) a.src_expert_off[(size_t)s * a.E + key] = pre;
+            }
+        }
+    }
+    __syncthreads();
+    if (!single && tid == 0) {
+        // this tile's boundary prefixes are visible to later tiles from here on
+        __threadfence();
+        __hip_atomic_store(a.bp_ready + tile, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+
+    // 4. stable rank of each kept slot: tokens before it in earlier tiles,
+    //    earlier waves of this tile, and earlier lanes of its wave
+    if (t < a.T) {
+        const uint64_t below = bit - 1;
+        int r[KMAX];
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) {
+            const int e = ev[j];
+            r[j] = e >= 0 ? excl[e] + wpre[wave * K + e] + __popcll(masks[wave * K + e] & below) : -1;
+        }
+        int32_t *rie = a.rank_in_expert + (size_t)t * a.k;
+        if ((a.k & 3) == 0) {
+#pragma unroll
+            for (int j = 0; j < KMAX; j += 4)
+                if (j < a.k) *reinterpret_cast<int4 *>(rie + j) = make_int4(r[j], r[j + 1], r[j + 2], r[j + 3]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < KMAX; ++j)
+                if (j < a.k) rie[j] = r[j];
+        }
+    }
+
+    // 5. per-source counts for the source ranks that end in this tile
+    //    (source s = tokens [s*T/R, (s+1)*T/R)); a start boundary owned by an
+    //    earlier tile is read back once that tile has published its prefixes
+    if (!single) {
+        int remote = -1;  // the one earlier tile whose boundary this tile may need
+        for (int s = 0; s < a.R; ++s) {
+            if (boundary_owner((s + 1) * a.tpr, a.T, a.num_tiles) != tile) continue;
+            const int o = boundary_owner(s * a.tpr, a.T, a.num_tiles);
+            if (o != tile) remote = o;
+        }
+        if (remote >= 0) {
+            if (tid == 0) {
+                uint32_t spins = 0;
+                while (__hip_atomic_load(a.bp_ready + remote, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != epoch) {
+                    if (++spins > a.spin_limit) {
+                        atomicOr(&a.counters[kStatus], kStTimeout);
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(1);
+                }
+                __threadfence();
+            }
+            __syncthreads();
+        }
+        for (int s = 0; s < a.R; ++s) {
+            const int bhi = (s + 1) * a.tpr;
+            if (boundary_owner(bhi, a.T, a.num_tiles) != tile) continue;
+            const int blo = s * a.tpr;
+            const bool local_lo = boundary_owner(blo, a.T, a.num_tiles) == tile;
+            for (int key = tid; key < K; key += kTileTokens) {
+                const int hi = excl[key] + count_before(masks, wpre, K, key, bhi - t0, ntile);
+                const int lo = local_lo ? excl[key] + count_before(masks, wpre, K, key, blo - t0, ntile)
+                                        : __hip_atomic_load(a.bp + (size_t)s * K + key, __ATOMIC_RELAXED,
+                                                            __HIP_MEMORY_SCOPE_AGENT);
+                if (key < a.E)
+                    a.cnt_se[(size_t)s * a.E + key] = hi - lo;
+                else
+                    a.cnt_sd[(size_t)s * a.R + (key - a.E)] = hi - lo;
+            }
+        }
+    }
+
+    // 6. the last tile holds every key's total: rows per expert, expert
+    //    offsets inside each rank (block scan), rows per rank
+    if (last_tile) {
+        __syncthreads();  // wpre is reused as the scan array below
+        const int chunk = (a.E + kTileTokens - 1) / kTileTokens;
+        const int lo = min(tid * chunk, a.E), hi = min(lo + chunk, a.E);
+        int local = 0;
+        for (int e = lo; e < hi; ++e) local += excl[e] + agg[e];
+        int total;
+        int run = block_exclusive_scan(local, s_part, &total);
+        for (int e = lo; e < hi; ++e) {
+            scan[e] = run;
+            run += excl[e] + agg[e];
+        }
+        if (tid == 0) scan[a.E] = total;
+        __syncthreads();
+        for (int e = tid; e < a.E; e += kTileTokens) {
+            a.recv_cnt[e] = excl[e] + agg[e];
+            a.expert_off[e] = scan[e] - scan[(e / a.epr) * a.epr];
+        }
+        for (int d = tid; d < a.R; d += kTileTokens) {
+            const int rows = scan[(d + 1) * a.epr] - scan[d * a.epr];
+            a.rank_rows[d] = rows;
+            if ((int64_t)rows > a.cap_rows) atomicOr(&a.counters[kStatus], kStCap);
+        }
+    }
+
+    // 7. the last tile to finish re-arms the workspace for the next call
+    if (!single && tid == 0) {
+        if (atomicAdd(&a.counters[kDone], 1u) == (unsigned)a.num_tiles - 1) {
+            uint32_t ne = (epoch + 1u) & ((1u << 30) - 1u);
+            if (ne == 0) ne = 1;
+            __hip_atomic_store(&a.counters[kTicket], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&a.counters[kDone], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&a.counters[kEpoch], ne, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dispatch
+// ---------------------------------------------------------------------------
+
+// Slot j's receive row lives in lane j (lanes >= k hold -1).
+template <bool FWD>
+__device__ __forceinline__ int slot_row(const DispatchArgs &a, int t, int lane, int part) {
+    int p = -1;
+    if (lane < a.k) {
+        const size_t i = (size_t)t * a.k + lane;
+        if (FWD) {
+            const int e = a.topk[i];
+            const int r = a.rank_in_expert[i];
+            if (r >= 0 && e >= 0 && e < a.E) {
+                const int64_t local = (int64_t)a.expert_off[e] + r;
+                if (local < a.cap_rows) p = (int)((int64_t)(e / a.epr) * a.cap_rows + local);
+            }
+            if (part == 0) {
+                a.pos[i] = p;
+                if (p >= 0) {
+                    a.src_idx[p] = t;
+                    if (a.recv_w) a.recv_w[p] = a.w[i];
+                }
+            }
+        } else {
+            p = a.pos[i];
+            if (p < -1 || p >= a.num_rows) {  // not a position this buffer holds
+                atomicOr(&a.counters[kStatus], kStBadHandle);
+                p = -1;
+            }
+        }
+    }
+    return p;
+}
+
+template <bool FP8, bool FWD>
+__global__ __launch_bounds__(kWavesPerBlock * 64) void k_dispatch(DispatchArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int gw = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+    const int t = gw / a.waves_per_token;
+    const int part = gw - t * a.waves_per_token;
+    if (t >= a.T) return;  // whole wave
+
+    const int pass0 = part * a.passes_per_wave;
+    const int np = min(a.passes_per_wave, a.npass - pass0);
+    const int H = a.H;
+    const uint16_t *xrow = a.x + (size_t)t * H;
+
+    // issue every load of this wave's passes first (read-once: non-temporal);
+    // the slot rows are looked up while they are in flight
+    u32x4 v[2 * kMaxPassPerWave];
+#pragma unroll
+    for (int i = 0; i < kMaxPassPerWave; ++i) {
+        v[2 * i] = 0;
+        v[2 * i + 1] = 0;
+        if (i < np) {
+            const int ps = pass0 + i;
+            if (FP8) {
+                const int c = ps * 1024 + lane * 16;  // 16 channels per lane
+                if (c < H) {
+                    const u32x4 *src = reinterpret_cast<const u32x4 *>(xrow + c);
+                    v[2 * i] = __builtin_nontemporal_load(src);
+                    v[2 * i + 1] = __builtin_nontemporal_load(src + 1);
+                }
+            } else {
+                const int c0 = ps * 1024 + lane * 8;  // 8 channels per vector, lanes contiguous
+                if (c0 < H) v[2 * i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(xrow + c0));
+                if (c0 + 512 < H)
+                    v[2 * i + 1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(xrow + c0 + 512));
+            }
+        }
+    }
+
+    const int p = slot_row<FWD>(a, t, lane, part);
+
+    // receive rows are written with ordinary (cache-allocating) stores: on
+    // gfx950 they sustain a higher write rate than non-temporal ones here
+#pragma unroll
+    for (int i = 0; i < kMaxPassPerWave; ++i) {
+        if (i >= np) break;
+        const int ps = pass0 + i;
+        if (FP8) {
+            const int c = ps * 1024 + lane * 16;
+            float f[16];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const u32x4 u = v[2 * i + h];
+                f[8 * h + 0] = bf16_lo(u.x);
+                f[8 * h + 1] = bf16_hi(u.x);
+                f[8 * h + 2] = bf16_lo(u.y);
+                f[8 * h + 3] = bf16_hi(u.y);
+                f[8 * h + 4] = bf16_lo(u.z);
+                f[8 * h + 5] = bf16_hi(u.z);
+                f[8 * h + 6] = bf16_lo(u.w);
+                f[8 * h + 7] = bf16_hi(u.w);
+            }
+            // group of 128 channels = 8 consecutive lanes: reduce amax with
+            // quad_perm [1,0,3,2], quad_perm [2,3,0,1] and row_half_mirror
+            float m = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(f[e]));
+            m = dpp_max<0xB1>(m);
+            m = dpp_max<0x4E>(m);
+            m = dpp_max<0x141>(m);
+            const float am = fmaxf(m, 1e-4f);
+            const float inv = 448.0f / am;   // IEEE division
+            const float scale = am / 448.0f; // IEEE division
+            uint32_t q[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float y0 = fminf(fmaxf(f[4 * e + 0] * inv, -448.0f), 448.0f);
+                const float y1 = fminf(fmaxf(f[4 * e + 1] * inv, -448.0f), 448.0f);
+                const float y2 = fminf(fmaxf(f[4 * e + 2] * inv, -448.0f), 448.0f);
+                const float y3 = fminf(fmaxf(f[4 * e + 3] * inv, -448.0f), 448.0f);
+                int w = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
+                w = __builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, w, true);
+                q[e] = (uint32_t)w;
+            }
+            const u32x4 qv = {q[0], q[1], q[2], q[3]};
+            const bool act = c < H;
+            const int G = H >> 7;
+            uint8_t *rx = static_cast<uint8_t *>(a.recv_x);
+            for (int j = 0; j < a.k; ++j) {
+                const int pj = readlane_i(p, j);
+                if (pj < 0) continue;
+                if (act) {
+                    *reinterpret_cast<u32x4 *>(rx + (size_t)pj * H + c) = qv;
+                    if ((lane & 7) == 0) a.recv_scales[(size_t)pj * G + (c >> 7)] = scale;
+                }
+            }
+        } else {
+            const int c0 = ps * 1024 + lane * 8;
+            const bool a0 = c0 < H, a1 = c0 + 512 < H;
+            uint16_t *rx = static_cast<uint16_t *>(a.recv_x);
+            for (int j = 0; j < a.k; ++j) {
+                const int pj = readlane_i(p, j);
+                if (pj < 0) continue;
+                uint16_t *dst = rx + (size_t)pj * H + c0;
+                if (a0) *reinterpret_cast<u32x4 *>(dst) = v[2 * i];
+                if (a1) *reinterpret_cast<u32x4 *>(dst + 512) = v[2 * i + 1];
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// combine
+// ---------------------------------------------------------------------------
+
+constexpr int kSlotChunk = 8;
+
+template <bool OUT_F32>
+__global__ __launch_bounds__(kWavesPerBlock * 64) void k_combine(CombineArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int gw = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+    const int t = gw / a.waves_per_token;
+    const int part = gw - t * a.waves_per_token;
+    if (t >= a.T) return;
+
+    int p = -1;
+    float wt = 1.0f;
+    if (lane < a.k) {
+        p = a.pos[(size_t)t * a.k + lane];
+        if (p < -1 || p >= a.num_rows) {  // not a position this buffer holds
+            atomicOr(&a.counters[kStatus], kStBadHandle);
+            p = -1;
+        }
+        if (a.w) wt = a.w[(size_t)t * a.k + lane];
+    }
+    const int H = a.H;
+    const int pass0 = part * a.passes_per_wave;
+    const int pass1 = min(pass0 + a.passes_per_wave, a.npass);
+
+    for (int ps = pass0; ps < pass1; ++ps) {
+        const int c0 = ps * 1024 + lane * 8;  // channels c0..c0+7 and c0+512..c0+519
+        const bool a0 = c0 < H, a1 = c0 + 512 < H;
+        float acc0[8], acc1[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            acc0[e] = 0.0f;
+            acc1[e] = 0.0f;
+        }
+        for (int jb = 0; jb < a.k; jb += kSlotChunk) {
+            u32x4 r0[kSlotChunk], r1[kSlotChunk];
+            int pj[kSlotChunk];
+            float wj[kSlotChunk];
+#pragma unroll
+            for (int jj = 0; jj < kSlotChunk; ++jj) {
+                const int j = jb + jj;
+                pj[jj] = j < a.k ? readlane_i(p, j) : -1;
+                wj[jj] = readlane_f(wt, j & 63);
+                r0[jj] = 0;
+                r1[jj] = 0;
+                if (pj[jj] >= 0) {
+                    const uint16_t *src = a.rows + (size_t)pj[jj] * H + c0;
+                    if (a0) r0[jj] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src));
+                    if (a1) r1[jj] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src + 512));
+                }
+            }
+#pragma unroll
+            for (int jj = 0; jj < kSlotChunk; ++jj) {
+                if (pj[jj] < 0) continue;
+                const float w = wj[jj];
+                const u32x4 u = r0[jj], z = r1[jj];
+                acc0[0] = __builtin_fmaf(w, bf16_lo(u.x), acc0[0]);
+                acc0[1] = __builtin_fmaf(w, bf16_hi(u.x), acc0[1]);
+                acc0[2] = __builtin_fmaf(w, bf16_lo(u.y), acc0[2]);
+                acc0[3] = __builtin_fmaf(w, bf16_hi(u.y), acc0[3]);
+                acc0[4] = __builtin_fmaf(w, bf16_lo(u.z), acc0[4]);
+                acc0[5] = __builtin_fmaf(w, bf16_hi(u.z), acc0[5]);
+                acc0[6] = __builtin_fmaf(w, bf16_lo(u.w), acc0[6]);
+                acc0[7] = __builtin_fmaf(w, bf16_hi(u.w), acc0[7]);
+                acc1[0] = __builtin_fmaf(w, bf16_lo(z.x), acc1[0]);
+                acc1[1] = __builtin_fmaf(w, bf16_hi(z.x), acc1[1]);
+                acc1[2] = __builtin_fmaf(w, bf16_lo(z.y), acc1[2]);
+                acc1[3] = __builtin_fmaf(w, bf16_hi(z.y), acc1[3]);
+                acc1[4] = __builtin_fmaf(w, bf16_lo(z.z), acc1[4]);
+                acc1[5] = __builtin_fmaf(w, bf16_hi(z.z), acc1[5]);
+                acc1[6] = __builtin_fmaf(w, bf16_lo(z.w), acc1[6]);
+                acc1[7] = __builtin_fmaf(w, bf16_hi(z.w), acc1[7]);
+            }
+        }
+        if (OUT_F32) {
+            float *out = static_cast<float *>(a.out) + (size_t)t * H + c0;
+            if (a0) {
+                u32x4 o0 = {__float_as_uint(acc0[0]), __float_as_uint(acc0[1]), __float_as_uint(acc0[2]),
+                            __float_as_uint(acc0[3])};
+                u32x4 o1 = {__float_as_uint(acc0[4]), __float_as_uint(acc0[5]), __float_as_uint(acc0[6]),
+                            __float_as_uint(acc0[7])};
+                reinterpret_cast<u32x4 *>(out)[0] = o0;
+                reinterpret_cast<u32x4 *>(out)[1] = o1;
+            }
+            if (a1) {
+                u32x4 o0 = {__float_as_uint(acc1[0]), __float_as_uint(acc1[1]), __float_as_uint(acc1[2]),
+                            __float_as_uint(acc1[3])};
+                u32x4 o1 = {__float_as_uint(acc1[4]), __float_as_uint(acc1[5]), __float_as_uint(acc1[6]),
+                            __float_as_uint(acc1[7])};
+                reinterpret_cast<u32x4 *>(out + 512)[0] = o0;
+                reinterpret_cast<u32x4 *>(out + 512)[1] = o1;
+            }
+        } else {
+            uint16_t *out = static_cast<uint16_t *>(a.out) + (size_t)t * H + c0;
+            if (a0) {
+                const u32x4 o = {bf16_rne(acc0[0]) | (bf16_rne(acc0[1]) << 16),
+                                 bf16_rne(acc0[2]) | (bf16_rne(acc0[3]) << 16),
+                                 bf16_rne(acc0[4]) | (bf16_rne(acc0[5]) << 16),
+                                 bf16_rne(acc0[6]) | (bf16_rne(acc0[7]) << 16)};
+                __builtin_nontemporal_store(o, reinterpret_cast<u32x4 *>(out));
+            }
+            if (a1) {
+                const u32x4 o = {bf16_rne(acc1[0]) | (bf16_rne(acc1[1]) << 16),
+                                 bf16_rne(acc1[2]) | (bf16_rne(acc1[3]) << 16),
+                                 bf16_rne(acc1[4]) | (bf16_rne(acc1[5]) << 16),
+                                 bf16_rne(acc1[6]) | (bf16_rne(acc1[7]) << 16)};
+                __builtin_nontemporal_store(o, reinterpret_cast<u32x4 *>(out + 512));
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// copy
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void k_copy(const u32x4 *__restrict__ src, u32x4 *__restrict__ dst, size_t n) {
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+        __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+}
+
+}  // namespace
+
+hipError_t launch_layout(const LayoutArgs &a, hipStream_t s) {
+    const size_t lds = layout_lds_bytes(a.E + a.R);
+    if (a.k <= 8)
+        hipLaunchKernelGGL(k_layout<8>, dim3(a.num_tiles), dim3(kTileTokens), lds, s, a);
+    else
+        hipLaunchKernelGGL(k_layout<kMaxTopk>, dim3(a.num_tiles), dim3(kTileTokens), lds, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_dispatch(const DispatchArgs &a, bool fp8, bool forward, int num_waves, hipStream_t s) {
+    const dim3 grid((num_waves + kWavesPerBlock - 1) / kWavesPerBlock), block(kWavesPerBlock * 64);
+    if (fp8 && forward)
+        hipLaunchKernelGGL((k_dispatch<true, true>), grid, block, 0, s, a);
+    else if (fp8)
+        hipLaunchKernelGGL((k_dispatch<true, false>), grid, block, 0, s, a);
+    else if (forward)
+        hipLaunchKernelGGL((k_dispatch<false, true>), grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL((k_dispatch<false, false>), grid, block, 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_combine(const CombineArgs &a, bool out_f32, int num_waves, hipStream_t s) {
+    const dim3 grid((num_waves + kWavesPerBlock - 1) / kWavesPerBlock), block(kWavesPerBlock * 64);
+    if (out_f32)
+        hipLaunchKernelGGL(k_combine<true>, grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL(k_combine<false>, grid, block, 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_copy(const void *src, void *dst, size_t n16, hipStream_t s) {
+    const size_t want = (n16 + 255) / 256;
+    const unsigned blocks = (unsigned)(want < 256 * 64 ? (want ? want : 1) : 256 * 64);
+    hipLaunchKernelGGL(k_copy, dim3(blocks), dim3(256), 0, s, static_cast<const u32x4 *>(src),
+                       static_cast<u32x4 *>(dst), n16);
+    return hipGetLastError();
+}
+
+}  // namespace ep

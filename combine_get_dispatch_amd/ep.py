@@ -1,0 +1,340 @@
+"""ctypes binding of libep.so (include/ep.h), plus a thin torch-tensor wrapper.
+
+The functions ``ep_*`` mirror the C ABI one to one and take raw device
+pointers (ints). ``Buffer`` allocates the caller-owned layout / handle /
+receive tensors with torch and passes their pointers and torch's current HIP
+stream; it does no arithmetic of its own. Every step of the hot path runs in
+libep.so's kernels: if the library is missing, ``load()`` raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libep.so")
+
+EP_OK = 0
+EP_ERR_ARG = -1
+EP_ERR_ALIGN = -2
+EP_ERR_HIP = -3
+EP_ERR_NOMEM = -4
+
+EP_ST_BAD_EXPERT = 1
+EP_ST_DUP_EXPERT = 2
+EP_ST_CAPACITY = 4
+EP_ST_TIMEOUT = 8
+EP_ST_BAD_HANDLE = 16
+
+c_void_p = ctypes.c_void_p
+
+
+class EpConfig(ctypes.Structure):
+    _fields_ = [("num_tokens", ctypes.c_int32), ("num_topk", ctypes.c_int32),
+                ("num_experts", ctypes.c_int32), ("num_ranks", ctypes.c_int32),
+                ("hidden", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("cap_rows", ctypes.c_int64)]
+
+
+LAYOUT_FIELDS = ("cnt_se", "cnt_sd", "recv_cnt", "expert_off", "rank_rows", "src_expert_off",
+                 "rank_in_expert", "is_token_in_rank")
+
+
+class EpLayout(ctypes.Structure):
+    _fields_ = [(n, c_void_p) for n in LAYOUT_FIELDS]
+
+
+class EpHandle(ctypes.Structure):
+    _fields_ = [("pos", c_void_p), ("src_idx", c_void_p),
+                ("num_tokens", ctypes.c_int32), ("num_topk", ctypes.c_int32)]
+
+
+SIZE_FIELDS = ("cnt_se", "cnt_sd", "recv_cnt", "expert_off", "rank_rows", "src_expert_off",
+               "rank_in_expert", "is_token_in_rank", "pos", "src_idx", "x", "recv_x_bf16",
+               "recv_x_fp8", "recv_scales", "recv_w", "combined_x", "workspace")
+
+
+class EpSizes(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in SIZE_FIELDS]
+
+
+# (name, restype, argtypes) for every symbol include/ep.h declares
+SIGNATURES = {
+    "ep_version": (ctypes.c_int, []),
+    "ep_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+    "ep_query_sizes": (ctypes.c_int, [ctypes.POINTER(EpConfig), ctypes.POINTER(EpSizes)]),
+    "ep_create": (ctypes.c_int, [ctypes.POINTER(EpConfig), ctypes.POINTER(c_void_p)]),
+    "ep_destroy": (ctypes.c_int, [c_void_p]),
+    "ep_get_dispatch_layout": (ctypes.c_int, [c_void_p, c_void_p, ctypes.POINTER(EpLayout), c_void_p]),
+    "ep_dispatch": (ctypes.c_int, [c_void_p, c_void_p, c_void_p, c_void_p, ctypes.POINTER(EpLayout),
+                                   ctypes.c_int, c_void_p, c_void_p, c_void_p,
+                                   ctypes.POINTER(EpHandle), c_void_p]),
+    "ep_combine": (ctypes.c_int, [c_void_p, c_void_p, ctypes.POINTER(EpHandle), c_void_p, c_void_p,
+                                  c_void_p]),
+    "ep_combine_f32": (ctypes.c_int, [c_void_p, c_void_p, ctypes.POINTER(EpHandle), c_void_p,
+                                      c_void_p, c_void_p]),
+    "ep_combine_backward": (ctypes.c_int, [c_void_p, c_void_p, ctypes.POINTER(EpHandle), c_void_p,
+                                           c_void_p]),
+    "ep_dispatch_backward": (ctypes.c_int, [c_void_p, c_void_p, ctypes.POINTER(EpHandle), c_void_p,
+                                            c_void_p, c_void_p]),
+    "ep_get_status": (ctypes.c_int, [c_void_p, c_void_p, ctypes.POINTER(ctypes.c_uint32)]),
+    "ep_copy_bytes": (ctypes.c_int, [c_void_p, c_void_p, ctypes.c_size_t, c_void_p]),
+}
+
+_lib = None
+
+
+class EpError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        self.code = code
+        super().__init__(f"{what}: {ep_strerror(code)} ({code})")
+
+
+def load():
+    """Load libep.so (built in-tree by combine_get_dispatch_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libep.so not built ({LIB_PATH}); run "
+                               "`python -m combine_get_dispatch_amd.build` or __graft_entry__.build()")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def _check(code: int, what: str) -> None:
+    if code != EP_OK:
+        raise EpError(code, what)
+
+
+# ---------------------------------------------------------------------------
+# the C ABI, one function per symbol
+# ---------------------------------------------------------------------------
+
+def ep_version() -> int:
+    return load().ep_version()
+
+
+def ep_strerror(code: int) -> str:
+    return load().ep_strerror(code).decode()
+
+
+def ep_query_sizes(cfg: EpConfig) -> EpSizes:
+    s = EpSizes()
+    _check(load().ep_query_sizes(ctypes.byref(cfg), ctypes.byref(s)), "ep_query_sizes")
+    return s
+
+
+def ep_create(cfg: EpConfig) -> int:
+    ctx = c_void_p()
+    _check(load().ep_create(ctypes.byref(cfg), ctypes.byref(ctx)), "ep_create")
+    return ctx.value
+
+
+def ep_destroy(ctx: int) -> None:
+    _check(load().ep_destroy(ctx), "ep_destroy")
+
+
+def ep_get_dispatch_layout(ctx: int, topk_idx: int, layout: EpLayout, stream: int) -> None:
+    _check(load().ep_get_dispatch_layout(ctx, topk_idx, ctypes.byref(layout), stream),
+           "ep_get_dispatch_layout")
+
+
+def ep_dispatch(ctx: int, x: int, topk_idx: int, topk_weights: Optional[int], layout: EpLayout,
+                use_fp8: int, recv_x: int, recv_scales: Optional[int], recv_w: Optional[int],
+                handle: EpHandle, stream: int) -> None:
+    _check(load().ep_dispatch(ctx, x, topk_idx, topk_weights, ctypes.byref(layout), int(use_fp8),
+                              recv_x, recv_scales, recv_w, ctypes.byref(handle), stream), "ep_dispatch")
+
+
+def ep_combine(ctx: int, expert_out: int, handle: EpHandle, weights: Optional[int],
+               combined_x: int, stream: int) -> None:
+    _check(load().ep_combine(ctx, expert_out, ctypes.byref(handle), weights, combined_x, stream),
+           "ep_combine")
+
+
+def ep_combine_f32(ctx: int, expert_out: int, handle: EpHandle, weights: Optional[int],
+                   combined_f32: int, stream: int) -> None:
+    _check(load().ep_combine_f32(ctx, expert_out, ctypes.byref(handle), weights, combined_f32, stream),
+           "ep_combine_f32")
+
+
+def ep_combine_backward(ctx: int, grad_combined: int, handle: EpHandle, grad_rows: int,
+                        stream: int) -> None:
+    _check(load().ep_combine_backward(ctx, grad_combined, ctypes.byref(handle), grad_rows, stream),
+           "ep_combine_backward")
+
+
+def ep_dispatch_backward(ctx: int, grad_rows: int, handle: EpHandle, weights: Optional[int],
+                         grad_x: int, stream: int) -> None:
+    _check(load().ep_dispatch_backward(ctx, grad_rows, ctypes.byref(handle), weights, grad_x, stream),
+           "ep_dispatch_backward")
+
+
+def ep_get_status(ctx: int, stream: int) -> int:
+    st = ctypes.c_uint32()
+    _check(load().ep_get_status(ctx, stream, ctypes.byref(st)), "ep_get_status")
+    return st.value
+
+
+def ep_copy_bytes(src: int, dst: int, nbytes: int, stream: int) -> None:
+    _check(load().ep_copy_bytes(src, dst, nbytes, stream), "ep_copy_bytes")
+
+
+# ---------------------------------------------------------------------------
+# torch convenience layer (allocation + pointer marshalling only)
+# ---------------------------------------------------------------------------
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream() -> int:
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+@dataclass
+class Layout:
+    cnt_se: "torch.Tensor"
+    cnt_sd: "torch.Tensor"
+    recv_cnt: "torch.Tensor"
+    expert_off: "torch.Tensor"
+    rank_rows: "torch.Tensor"
+    src_expert_off: "torch.Tensor"
+    rank_in_expert: "torch.Tensor"
+    is_token_in_rank: "torch.Tensor"
+
+    def c(self) -> EpLayout:
+        return EpLayout(*[getattr(self, n).data_ptr() for n in LAYOUT_FIELDS])
+
+
+@dataclass
+class Handle:
+    pos: "torch.Tensor"       # [T, k] int32
+    src_idx: "torch.Tensor"   # [R * cap_rows] int32
+    num_tokens: int = 0
+    num_topk: int = 0
+
+    def c(self) -> EpHandle:
+        return EpHandle(self.pos.data_ptr(), self.src_idx.data_ptr(), self.num_tokens, self.num_topk)
+
+
+class Buffer:
+    """One expert-parallel group collapsed onto the current GPU: the analogue
+    of the DeepEP guide's buffer (created once for a token count, hidden size
+    and top-k), holding the libep context."""
+
+    def __init__(self, num_tokens: int, hidden: int, num_topk: int, num_experts: int,
+                 num_ranks: int, cap_rows: int, device=None):
+        import torch
+        self.torch = torch
+        self.device = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+        self.cfg = EpConfig(num_tokens, num_topk, num_experts, num_ranks, hidden, 0, int(cap_rows))
+        self.sizes = ep_query_sizes(self.cfg)
+        with torch.cuda.device(self.device):
+            self.ctx = ep_create(self.cfg)
+
+    # sizes
+    @property
+    def T(self): return self.cfg.num_tokens
+
+    @property
+    def k(self): return self.cfg.num_topk
+
+    @property
+    def E(self): return self.cfg.num_experts
+
+    @property
+    def R(self): return self.cfg.num_ranks
+
+    @property
+    def H(self): return self.cfg.hidden
+
+    @property
+    def cap_rows(self): return self.cfg.cap_rows
+
+    @property
+    def num_rows(self): return self.R * self.cap_rows
+
+    def close(self):
+        if getattr(self, "ctx", None):
+            ep_destroy(self.ctx)
+            self.ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def _empty(self, shape, dtype):
+        return self.torch.empty(shape, dtype=dtype, device=self.device)
+
+    def new_layout(self) -> Layout:
+        t = self.torch
+        T, k, E, R = self.T, self.k, self.E, self.R
+        return Layout(self._empty((R, E), t.int32), self._empty((R, R), t.int32), self._empty(E, t.int32),
+                      self._empty(E, t.int32), self._empty(R, t.int32), self._empty((R, E), t.int32),
+                      self._empty((T, k), t.int32), self._empty((T, R), t.uint8))
+
+    def new_handle(self) -> Handle:
+        t = self.torch
+        return Handle(self._empty((self.T, self.k), t.int32), self._empty(self.num_rows, t.int32))
+
+    def get_dispatch_layout(self, topk_idx, layout: Optional[Layout] = None) -> Layout:
+        layout = layout or self.new_layout()
+        ep_get_dispatch_layout(self.ctx, topk_idx.data_ptr(), layout.c(), _stream())
+        return layout
+
+    def dispatch(self, x, topk_idx, topk_weights, layout: Layout, use_fp8: bool, out=None):
+        """Returns (recv_x, recv_scales, recv_w, handle)."""
+        t = self.torch
+        if out is None:
+            recv_x = self._empty((self.num_rows, self.H), t.uint8 if use_fp8 else t.bfloat16)
+            recv_scales = self._empty((self.num_rows, self.H // 128), t.float32) if use_fp8 else None
+            recv_w = self._empty(self.num_rows, t.float32)
+            handle = self.new_handle()
+        else:
+            recv_x, recv_scales, recv_w, handle = out
+        ch = handle.c()
+        ep_dispatch(self.ctx, x.data_ptr(), topk_idx.data_ptr(), _ptr(topk_weights), layout.c(),
+                    int(bool(use_fp8)), recv_x.data_ptr(), _ptr(recv_scales), _ptr(recv_w), ch, _stream())
+        handle.num_tokens, handle.num_topk = ch.num_tokens, ch.num_topk
+        return recv_x, recv_scales, recv_w, handle
+
+    def combine(self, expert_out, handle: Handle, weights=None, out=None):
+        out = out if out is not None else self._empty((self.T, self.H), self.torch.bfloat16)
+        ep_combine(self.ctx, expert_out.data_ptr(), handle.c(), _ptr(weights), out.data_ptr(), _stream())
+        return out
+
+    def combine_f32(self, expert_out, handle: Handle, weights=None, out=None):
+        out = out if out is not None else self._empty((self.T, self.H), self.torch.float32)
+        ep_combine_f32(self.ctx, expert_out.data_ptr(), handle.c(), _ptr(weights), out.data_ptr(), _stream())
+        return out
+
+    def combine_backward(self, grad_combined, handle: Handle, out=None):
+        out = out if out is not None else self._empty((self.num_rows, self.H), self.torch.bfloat16)
+        ep_combine_backward(self.ctx, grad_combined.data_ptr(), handle.c(), out.data_ptr(), _stream())
+        return out
+
+    def dispatch_backward(self, grad_rows, handle: Handle, weights=None, out=None):
+        out = out if out is not None else self._empty((self.T, self.H), self.torch.bfloat16)
+        ep_dispatch_backward(self.ctx, grad_rows.data_ptr(), handle.c(), _ptr(weights), out.data_ptr(),
+                             _stream())
+        return out
+
+    def status(self) -> int:
+        """Synchronize the current stream; return and clear the sticky status bits."""
+        return ep_get_status(self.ctx, _stream())
+
+
+def copy_bytes(src, dst) -> None:
+    n = min(src.numel() * src.element_size(), dst.numel() * dst.element_size())
+    ep_copy_bytes(src.data_ptr(), dst.data_ptr(), n, _stream())

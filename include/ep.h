@@ -1,0 +1,211 @@
+/* ep.h -- C ABI of libep.so: MoE expert-parallel dispatch / combine, the
+ * token exchange of DeepEP-style expert parallelism, on one MI355X (gfx950).
+ *
+ * What the calls compute. The DeepEP usage guide (zhouruolin.cn, "DeepEP：MoE
+ * 专家并行 EP 通信 kernel 编译与使用指南", section 5 "使用方法") gives the
+ * interface this ABI follows: a buffer created once for a maximum number of
+ * tokens per rank, hidden size and top-k; dispatch(x, topk_idx,
+ * topk_weights, num_experts, ...) returning the received activations, the
+ * received top-k weights and a handle; combine(expert_output, handle)
+ * returning the combined activations; and combine_backward /
+ * dispatch_backward reusing the forward handle. The launch report
+ * (czhn.yksolo.com, section on the normal kernels) and the blog.hotdry.top
+ * notes (section 5, precision choice) pair FP8 dispatch with BF16 combine.
+ * The pages do not define the layout step, the receive layout, the FP8 scale
+ * granularity or the combine arithmetic; the readings used here are stated at
+ * each call below.
+ *
+ * Expert-parallel group on one GPU. The R expert-parallel ranks are R
+ * disjoint partitions of this GPU's memory: receive rows
+ * [d*cap_rows, (d+1)*cap_rows) belong to rank d. Source tokens are split in
+ * contiguous blocks of T/R per source rank; expert e lives on rank e/(E/R).
+ *
+ * Conventions.
+ *  - All array arguments are DEVICE pointers to memory the caller owns
+ *    (allocated with hipMalloc or by torch); the library never frees them.
+ *    Struct arguments (ep_config, ep_layout, ep_handle, ep_sizes) are HOST
+ *    structs whose pointer fields are device pointers.
+ *  - Every compute call is asynchronous on `stream` (a hipStream_t passed as
+ *    void*; NULL = the legacy default stream) and returns once its kernels are
+ *    queued. Inputs must stay alive and unmodified until the stream has passed
+ *    the call.
+ *  - bf16 values are passed as uint16_t bit patterns, FP8 as OCP e4m3fn bytes,
+ *    weights and scales as IEEE fp32, routing indices as int32 with -1 meaning
+ *    "no expert in this slot". All arrays are row-major and dense.
+ *  - A negative return value means nothing was launched (EP_ERR_*).
+ *    Data-dependent problems (bad expert ids, capacity overflow) are reported
+ *    through sticky device status bits (EP_ST_*, read with ep_get_status); the
+ *    kernels never write outside the caller's buffers when one is raised.
+ *  - One ep_ctx holds a small device workspace used by the layout kernel;
+ *    calls on the same ctx must be ordered on one stream (calls on different
+ *    streams that use the same ctx at the same time race).
+ */
+#ifndef EP_H
+#define EP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define EP_ABI_VERSION 1
+
+/* return codes */
+#define EP_OK 0
+#define EP_ERR_ARG (-1)   /* invalid config, null pointer, size mismatch, handle from another config */
+#define EP_ERR_ALIGN (-2) /* a row array is not 16-byte aligned */
+#define EP_ERR_HIP (-3)   /* a HIP runtime call failed */
+#define EP_ERR_NOMEM (-4) /* the workspace could not be allocated */
+
+/* sticky device status bits */
+#define EP_ST_BAD_EXPERT 1u /* an index outside [-1, E): that slot was dropped */
+#define EP_ST_DUP_EXPERT 2u /* an expert repeated within a token: repeats after the first were dropped */
+#define EP_ST_CAPACITY 4u   /* a rank needs more than cap_rows rows: rows past cap_rows were dropped */
+#define EP_ST_TIMEOUT 8u    /* the layout scan gave up waiting for a predecessor tile (results invalid) */
+#define EP_ST_BAD_HANDLE 16u /* a handle position outside [-1, R*cap_rows): that slot was skipped */
+
+typedef void *ep_stream_t;
+typedef struct ep_ctx ep_ctx;
+
+/* Problem size, fixed when the context is created (the guide's buffer is
+ * created for a maximum token count, hidden size and top-k).
+ * Limits: 0 <= num_tokens <= 2^24, num_tokens % num_ranks == 0;
+ * 1 <= num_topk <= 32; 1 <= num_ranks <= 64; 1 <= num_experts <= 1024,
+ * num_experts % num_ranks == 0; 8 <= hidden <= 65536, hidden % 8 == 0
+ * (hidden % 128 == 0 for FP8 dispatch); 0 <= cap_rows,
+ * num_ranks * cap_rows < 2^31. */
+typedef struct {
+    int32_t num_tokens;  /* T: source tokens on this GPU, all simulated source ranks together */
+    int32_t num_topk;    /* k: expert slots per token */
+    int32_t num_experts; /* E */
+    int32_t num_ranks;   /* R: simulated expert-parallel ranks */
+    int32_t hidden;      /* H: channels per token */
+    int32_t reserved;    /* must be 0 */
+    int64_t cap_rows;    /* receive rows per rank (the guide's per-rank token capacity) */
+} ep_config;
+
+/* Output of ep_get_dispatch_layout (caller-allocated device arrays). */
+typedef struct {
+    int32_t *cnt_se;          /* [R][E] tokens of source rank s routed to expert e */
+    int32_t *cnt_sd;          /* [R][R] tokens of source rank s with >= 1 expert on rank d */
+    int32_t *recv_cnt;        /* [E] rows expert e receives */
+    int32_t *expert_off;      /* [E] first row of expert e inside its rank's region */
+    int32_t *rank_rows;       /* [R] rows rank d receives (may exceed cap_rows: see EP_ST_CAPACITY) */
+    int32_t *src_expert_off;  /* [R][E] rows of expert e from source ranks < s: where source s's rows start
+                                 inside e's rows (absolute row: d*cap_rows + expert_off[e] + this) */
+    int32_t *rank_in_expert;  /* [T][k] number of earlier tokens routed to the same expert, -1 if the slot is dropped */
+    uint8_t *is_token_in_rank;/* [T][R] 1 if token t has an expert on rank d */
+} ep_layout;
+
+/* The routing state dispatch produces and combine / the backward pair reuse
+ * (caller-allocated device arrays; the integer fields are set by ep_dispatch). */
+typedef struct {
+    int32_t *pos;     /* [T][k] receive row of slot (t, j), or -1 if the slot is dropped */
+    int32_t *src_idx; /* [R*cap_rows] source token of each kept row; entries of unused rows are not written */
+    int32_t num_tokens, num_topk; /* the config the handle was made for (checked by its users) */
+} ep_handle;
+
+/* Byte sizes of every caller buffer for a config (host-only, no GPU needed). */
+typedef struct {
+    size_t cnt_se, cnt_sd, recv_cnt, expert_off, rank_rows, src_expert_off;
+    size_t rank_in_expert, is_token_in_rank, pos, src_idx;
+    size_t x, recv_x_bf16, recv_x_fp8, recv_scales, recv_w, combined_x;
+    size_t workspace; /* device bytes ep_create allocates */
+} ep_sizes;
+
+/* Version of this ABI (EP_ABI_VERSION). */
+int ep_version(void);
+
+/* Text for a return code (EP_OK / EP_ERR_*). Never NULL, static storage. */
+const char *ep_strerror(int code);
+
+/* Validate a config and report buffer sizes. Host only; does not touch the
+ * GPU. Returns EP_OK or EP_ERR_ARG (out may be NULL to validate only). */
+int ep_query_sizes(const ep_config *cfg, ep_sizes *out);
+
+/* Create a context on the current HIP device: validates cfg, allocates and
+ * zeroes the layout workspace (the only allocation the library makes; the
+ * guide's buffer is likewise created once and reused). *out is set on
+ * success. Returns EP_OK, EP_ERR_ARG, EP_ERR_NOMEM or EP_ERR_HIP. */
+int ep_create(const ep_config *cfg, ep_ctx **out);
+
+/* Free the workspace (synchronizes the device first). NULL is ignored. */
+int ep_destroy(ep_ctx *ctx);
+
+/* Dispatch layout from top-k routing (the step before the guide's dispatch;
+ * the pages do not describe it, so its outputs are defined here):
+ * per-expert and per-rank counts, the is-token-in-rank mask, and the stable
+ * per-expert scan: rank_in_expert[t][j] = number of tokens t' < t routed to
+ * the same expert, so every expert's rows are ordered by source token.
+ * Slot validation: -1 = empty; an index outside [-1, E) sets
+ * EP_ST_BAD_EXPERT and is dropped; a repeat of an expert already in the
+ * token sets EP_ST_DUP_EXPERT and is dropped. rank_rows[d] > cap_rows sets
+ * EP_ST_CAPACITY. One kernel launch; uses the ctx workspace.
+ * topk_idx: [T][k] int32. All layout pointers must be non-NULL (T = 0 allowed);
+ * rank_in_expert and is_token_in_rank 16-byte aligned, the others 4-byte. */
+int ep_get_dispatch_layout(ep_ctx *ctx, const int32_t *topk_idx, const ep_layout *layout,
+                           ep_stream_t stream);
+
+/* Dispatch (the guide's dispatch): for every kept slot (t, j) with expert e
+ * on rank d, writes handle->pos[t][j] = d*cap_rows + expert_off[e] +
+ * rank_in_expert[t][j] (slots whose row would fall at or past cap_rows are
+ * dropped: pos = -1), src_idx[pos] = t, recv_w[pos] = topk_weights[t][j] and
+ * the token's row:
+ *   use_fp8 = 0: recv_x [R*cap_rows][H] bf16, a bit copy of x[t];
+ *   use_fp8 = 1: recv_x [R*cap_rows][H] e4m3 bytes and
+ *     recv_scales [R*cap_rows][H/128] fp32: per group of 128 channels,
+ *     amax = max |x|, a = max(amax, 1e-4), scale = a/448, and
+ *     q = e4m3(x * (448/a)) rounded to nearest even, saturating at 448
+ *     (fp32 divisions and multiply, IEEE).
+ * x: [T][H] bf16; topk_idx, layout: as passed to ep_get_dispatch_layout;
+ * topk_weights: [T][k] fp32 (NULL: recv_w is not written; recv_w may be NULL).
+ * recv_x must be 16-byte aligned; recv_scales must be non-NULL iff use_fp8.
+ * Rows no slot maps to are not written. */
+int ep_dispatch(ep_ctx *ctx, const uint16_t *x, const int32_t *topk_idx,
+                const float *topk_weights, const ep_layout *layout, int use_fp8,
+                void *recv_x, float *recv_scales, float *recv_w, ep_handle *handle,
+                ep_stream_t stream);
+
+/* Combine (the guide's combine): weighted gather-reduce back to source-token
+ * order. For each token t and channel i: acc = +0.0f; for j = 0..k-1 with
+ * pos[t][j] >= 0: acc = fmaf(w[t][j], expert_out[pos[t][j]][i], acc) (w = 1
+ * when weights is NULL); combined_x[t][i] = bf16(acc), round to nearest even.
+ * expert_out: [R*cap_rows][H] bf16; weights: [T][k] fp32 or NULL;
+ * combined_x: [T][H] bf16. Pointers 16-byte aligned. */
+int ep_combine(ep_ctx *ctx, const uint16_t *expert_out, const ep_handle *handle,
+               const float *weights, uint16_t *combined_x, ep_stream_t stream);
+
+/* ep_combine with the fp32 sums written before rounding ([T][H] fp32), for
+ * checking the reduction itself. */
+int ep_combine_f32(ep_ctx *ctx, const uint16_t *expert_out, const ep_handle *handle,
+                   const float *weights, float *combined_f32, ep_stream_t stream);
+
+/* combine_backward (the guide: backward reuses the forward handle): the
+ * gradient of combined_x travels the dispatch routes, i.e. a bf16 dispatch
+ * of grad_combined [T][H] into grad_rows [R*cap_rows][H] reusing handle->pos
+ * (no weights, no src_idx / recv_w writes; rows no slot maps to untouched). */
+int ep_combine_backward(ep_ctx *ctx, const uint16_t *grad_combined, const ep_handle *handle,
+                        uint16_t *grad_rows, ep_stream_t stream);
+
+/* dispatch_backward (the guide: backward reuses the forward handle): a
+ * gather-reduce of the per-row gradients grad_rows [R*cap_rows][H] into
+ * grad_x [T][H], exactly ep_combine's arithmetic with `weights` (NULL = 1). */
+int ep_dispatch_backward(ep_ctx *ctx, const uint16_t *grad_rows, const ep_handle *handle,
+                         const float *weights, uint16_t *grad_x, ep_stream_t stream);
+
+/* Synchronize `stream`, return the sticky status bits in *status and clear
+ * them. Returns EP_OK or EP_ERR_HIP. */
+int ep_get_status(ep_ctx *ctx, ep_stream_t stream, uint32_t *status);
+
+/* Measurement utility: copy `bytes` (a multiple of 16, both pointers 16-byte
+ * aligned) with a plain streaming-copy kernel, used to calibrate memory
+ * counters and as the attainable-bandwidth reference. */
+int ep_copy_bytes(const void *src, void *dst, size_t bytes, ep_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EP_H */

@@ -34,7 +34,7 @@ _default = None
 def _compile(src: str, out: str) -> None:
     """gcc -O2 with contraction off: every multiply and add stays as written
     (fmaf() is the only fused operation, and it is called explicitly)."""
-    tmp = out + ".tmp"
+    tmp = f"{out}.{os.getpid()}.tmp"
     cmd = ["gcc", "-std=c99", "-O2", "-ffp-contract=off", "-fno-fast-math",
            "-fPIC", "-shared", "-Wall", "-Wextra", "-I", _HERE, "-o", tmp, src, "-lm"]
     subprocess.run(cmd, check=True)

@@ -172,8 +172,9 @@ static int slot_is_valid(const int32_t *row, int j, int E, uint32_t *status) {
  *   expert_off[e]         first row of expert e inside rank d(e)'s region
  *                         (experts of one rank stored in ascending id order)
  *   rank_rows[d]          rows rank d receives
- *   src_expert_off[s][e]  first row, inside d(e)'s region, of the rows that
- *                         source rank s sends to expert e
+ *   src_expert_off[s][e]  first row, counted from the start of expert e's
+ *                         rows, of the rows source rank s sends to e (the rows
+ *                         of e that come from source ranks before s)
  *   rank_in_expert[t][j]  number of tokens t' < t routed to the same expert:
  *                         the stable (by source token index) order of the
  *                         expert's rows; -1 for a slot that is not valid.
@@ -226,7 +227,7 @@ uint32_t oracle_layout(int T, int k, int E, int R, long long cap_rows,
     for (int e = 0; e < E; ++e) {
         int32_t before = 0; /* rows sent to e by source ranks s' < s */
         for (int s = 0; s < R; ++s) {
-            src_expert_off[(size_t)s * E + e] = expert_off[e] + before;
+            src_expert_off[(size_t)s * E + e] = before;
             before += cnt_se[(size_t)s * E + e];
         }
     }

@@ -204,7 +204,7 @@ def brute_layout(topk, E, R, cap):
     recv = np.array([sum(1 for t in range(T) if e in experts_of[t]) for e in range(E)])
     eoff = np.array([sum(int(recv[x]) for x in range((e // epr) * epr, e)) for e in range(E)])
     rrows = np.array([sum(int(recv[e]) for e in range(d * epr, (d + 1) * epr)) for d in range(R)])
-    seoff = np.array([[int(eoff[e]) + sum(int(cnt_se[sp, e]) for sp in range(s)) for e in range(E)]
+    seoff = np.array([[sum(int(cnt_se[sp, e]) for sp in range(s)) for e in range(E)]
                       for s in range(R)])
     if any(int(r) > cap for r in rrows):
         status |= 4
@@ -303,10 +303,10 @@ def check_layout_invariants(topk, E, R, cap, L, pos, src_idx):
     for ee in np.unique(e):
         rows = np.sort(p[e == ee])
         assert np.all(np.diff(src_idx[rows]) > 0), f"expert {ee} rows not in token order"
-    # src_expert_off: rows of (source rank s, expert e) start there
+    # src_expert_off: inside expert e's rows, those of source rank s start there
     tpr = T // R if T else 1
     for s_, ee, pp in zip(tok[valid] // tpr, e, local):
-        lo = L.src_expert_off[s_, ee]
+        lo = L.expert_off[ee] + L.src_expert_off[s_, ee]
         assert lo <= pp < lo + L.cnt_se[s_, ee]
 
 

@@ -32,8 +32,10 @@ MUTANTS = [
     ("expert offsets inclusive", "            expert_off[e] = off;\n            off += recv_cnt[e];",
      "            off += recv_cnt[e];\n            expert_off[e] = off - recv_cnt[e] + (recv_cnt[e] > 0);"),
     ("source offsets skip the current rank",
-     "            src_expert_off[(size_t)s * E + e] = expert_off[e] + before;\n            before += cnt_se[(size_t)s * E + e];",
-     "            before += cnt_se[(size_t)s * E + e];\n            src_expert_off[(size_t)s * E + e] = expert_off[e] + before;"),
+     "            src_expert_off[(size_t)s * E + e] = before;\n            before += cnt_se[(size_t)s * E + e];",
+     "            before += cnt_se[(size_t)s * E + e];\n            src_expert_off[(size_t)s * E + e] = before;"),
+    ("source offsets rank-relative", "            src_expert_off[(size_t)s * E + e] = before;",
+     "            src_expert_off[(size_t)s * E + e] = expert_off[e] + before;"),
     ("per-rank token count counts slots",
      "cnt_sd[(size_t)s * R + d] += is_token_in_rank[(size_t)t * R + d];",
      "cnt_sd[(size_t)s * R + d] += 2 * is_token_in_rank[(size_t)t * R + d];"),
