@@ -13,13 +13,14 @@ namespace ep {
 // exclusive prefix and count (4 B each).
 constexpr int kLayoutTile = 256;
 constexpr int kCoResidentTiles = 256;  // grids up to this size number tiles by block index
+constexpr int kLayoutReplicas = 8;     // blocks sharing the outputs of a single tile
 inline size_t layout_lds_bytes(int keys) { return (size_t)keys * (4 * 8 + 4 * 4 + 2 * 4); }
 constexpr int kMaxTopk = 32;
 constexpr int kMaxRanks = 64;
 constexpr int kMaxExperts = 1024;
 
 // ctx workspace counters (uint32 each)
-enum Counter { kTicket = 0, kDone = 1, kEpoch = 2, kStatus = 3, kNumCounters = 16 };
+enum Counter { kTicket = 0, kEpoch = 2, kStatus = 3, kNumCounters = 16 };
 
 struct LayoutArgs {
     const int32_t *topk;

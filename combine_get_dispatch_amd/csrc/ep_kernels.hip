@@ -66,7 +66,7 @@ __device__ __forceinline__ uint64_t pack_state(uint32_t epoch, uint64_t flag, ui
     return ((uint64_t)epoch << 34) | (flag << 32) | (uint64_t)v;
 }
 
-constexpr int kLookbackWindow = 16;  // predecessor states read per round trip
+constexpr int kLookbackWindow = 32;  // predecessor states read per round trip
 constexpr int kTileWaves = 4;
 constexpr int kTileTokens = kTileWaves * 64;
 
@@ -96,21 +96,37 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int *s_part, int *tot
     return s_part[wave] + x - v;
 }
 
-// Tokens of this tile before tile-local position nb that hold `key`
-// (wpre[w][key] = such tokens in waves before w).
-__device__ __forceinline__ int count_before(const uint64_t *masks, const int32_t *wpre, int K, int key, int nb,
-                                            int ntile) {
-    if (nb <= 0) return 0;
-    if (nb > ntile) nb = ntile;
-    const int w = nb >> 6, l = nb & 63;
-    if (w == kTileWaves) return wpre[(w - 1) * K + key] + __popcll(masks[(w - 1) * K + key]);
-    const int c = wpre[w * K + key];
-    return l ? c + __popcll(masks[w * K + key] & ((1ull << l) - 1)) : c;
+// One key's view of the tile, held in registers: the four wave masks.
+struct KeyView {
+    uint64_t m0, m1, m2, m3;
+};
+
+__device__ __forceinline__ KeyView key_view(const uint64_t *masks, int K, int key) {
+    KeyView v;
+    v.m0 = masks[key];
+    v.m1 = masks[K + key];
+    v.m2 = masks[2 * K + key];
+    v.m3 = masks[3 * K + key];
+    return v;
 }
 
-// Tile owning source-rank boundary b (token index; b == T is the end).
-__device__ __forceinline__ int boundary_owner(int b, int T, int num_tiles) {
-    return b < T ? b / kTileTokens : num_tiles - 1;
+// Lanes [0, n) of a wave as a mask (n clamped to [0, 64]).
+__device__ __forceinline__ uint64_t lanes_below(int n) {
+    return n <= 0 ? 0ull : n >= 64 ? ~0ull : ((1ull << n) - 1);
+}
+
+// Tokens of this tile before tile-local position nb that hold the key
+// (branch-free over the four waves, so the view stays in registers).
+__device__ __forceinline__ int count_before(const KeyView &v, int nb, int ntile) {
+    nb = min(nb, ntile);
+    return __popcll(v.m0 & lanes_below(nb)) + __popcll(v.m1 & lanes_below(nb - 64)) +
+           __popcll(v.m2 & lanes_below(nb - 128)) + __popcll(v.m3 & lanes_below(nb - 192));
+}
+
+// Four is_token_in_rank bytes (ranks d..d+3 of the mask, one byte each).
+__device__ __forceinline__ uint32_t rank_bytes4(uint64_t rmask, int d) {
+    const uint32_t x = (uint32_t)(rmask >> d) & 0xFu;
+    return (x & 1u) | ((x & 2u) << 7) | ((x & 4u) << 14) | ((x & 8u) << 21);
 }
 
 template <int KMAX>
@@ -126,16 +142,20 @@ __global__ __launch_bounds__(kTileTokens) void k_layout(LayoutArgs a) {
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const bool single = a.num_tiles == 1;
-    uint32_t epoch = 0;
-    if (!single) epoch = __hip_atomic_load(&a.counters[kEpoch], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
     // A tile only waits on lower-numbered tiles. Small grids are co-resident,
     // so the block index is the tile; larger grids number tiles in the order
     // they start (a ticket), so every predecessor is already running.
-    if (tid == 0) s_tile = a.use_ticket ? (int)atomicAdd(&a.counters[kTicket], 1u) : (int)blockIdx.x;
-    for (int i = tid; i < kTileWaves * K; i += kTileTokens) masks[i] = 0;
-    __syncthreads();
-    const int tile = s_tile;
+    // One tile: the grid is a few replicas of it, each writing a slice of the
+    // outputs (no cross-block traffic). Several tiles: block = tile.
+    const int replica = single ? (int)blockIdx.x : 0;
+    const int nrep = single ? (int)gridDim.x : 1;
+    int tile = single ? 0 : (int)blockIdx.x;
+    if (a.use_ticket) {
+        if (tid == 0) s_tile = (int)atomicAdd(&a.counters[kTicket], 1u);
+        __syncthreads();
+        tile = s_tile;
+    }
     if (tile >= a.num_tiles) {  // workspace not re-armed (an earlier call did not finish)
         if (tid == 0) atomicOr(&a.counters[kStatus], kStTimeout);
         return;
@@ -145,6 +165,32 @@ __global__ __launch_bounds__(kTileTokens) void k_layout(LayoutArgs a) {
     const int ntile = max(min(kTileTokens, a.T - t0), 0);  // tokens in this tile
     const bool last_tile = tile == a.num_tiles - 1;
     const uint64_t bit = 1ull << lane;
+    // Source rank s holds tokens [s*T/R, (s+1)*T/R). This tile writes the
+    // start offsets of the sources whose first token it holds, [first_lo,
+    // first_hi), and the counts of those whose last token it holds,
+    // [last_lo, last_hi); a source inside one tile needs nothing from others.
+    int first_lo = 0, first_hi = 0, last_lo = 0, last_hi = 0;
+    bool publish = false;  // a later tile ends a source that starts here
+    if (!single) {
+        first_lo = min((t0 + a.tpr - 1) / a.tpr, a.R);
+        first_hi = min((t0 + kTileTokens + a.tpr - 1) / a.tpr, a.R);
+        last_lo = min(t0 / a.tpr, a.R);
+        last_hi = min((t0 + kTileTokens) / a.tpr, a.R);
+        if (last_tile) last_hi = a.R;
+        publish = first_hi > first_lo && first_hi * a.tpr - 1 >= t0 + kTileTokens;
+    }
+
+    // the token's slots are requested first; their latency covers the setup
+    int raw[KMAX];
+    {
+        const int32_t *row = a.topk + (size_t)t * a.k;
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) raw[j] = (t < a.T && j < a.k) ? row[j] : -1;
+    }
+    uint32_t epoch = 0;
+    if (!single) epoch = __hip_atomic_load(&a.counters[kEpoch], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int i = tid; i < kTileWaves * K; i += kTileTokens) masks[i] = 0;
+    __syncthreads();
 
     // 1. validate the token's slots; expert bits go into the wave's masks
     //    (LDS atomics), the per-rank bits are wave ballots (no atomics: every
@@ -153,31 +199,24 @@ __global__ __launch_bounds__(kTileTokens) void k_layout(LayoutArgs a) {
     uint32_t st = 0;
     uint64_t rmask = 0;
 #pragma unroll
-    for (int j = 0; j < KMAX; ++j) ev[j] = -1;
-    if (t < a.T) {
-        const int32_t *row = a.topk + (size_t)t * a.k;
-        int raw[KMAX];
-#pragma unroll
-        for (int j = 0; j < KMAX; ++j) raw[j] = j < a.k ? row[j] : -1;
-#pragma unroll
-        for (int j = 0; j < KMAX; ++j) {
-            const int v = raw[j];
-            if (v == -1) continue;
-            if (v < -1 || v >= a.E) {
-                st |= kStBad;
-                continue;
-            }
-            bool dup = false;
-#pragma unroll
-            for (int jj = 0; jj < j; ++jj) dup |= (ev[jj] == v);
-            if (dup) {
-                st |= kStDup;
-                continue;
-            }
-            ev[j] = v;
-            atomicOr(reinterpret_cast<unsigned long long *>(&masks[wave * K + v]), (unsigned long long)bit);
-            rmask |= 1ull << (v / a.epr);
+    for (int j = 0; j < KMAX; ++j) {
+        ev[j] = -1;
+        const int v = raw[j];
+        if (v == -1) continue;
+        if (v < -1 || v >= a.E) {
+            st |= kStBad;
+            continue;
         }
+        bool dup = false;
+#pragma unroll
+        for (int jj = 0; jj < j; ++jj) dup |= (ev[jj] == v);
+        if (dup) {
+            st |= kStDup;
+            continue;
+        }
+        ev[j] = v;
+        atomicOr(reinterpret_cast<unsigned long long *>(&masks[wave * K + v]), (unsigned long long)bit);
+        rmask |= 1ull << (v / a.epr);
     }
     {
         uint64_t mine = 0;
@@ -187,39 +226,41 @@ __global__ __launch_bounds__(kTileTokens) void k_layout(LayoutArgs a) {
         }
         if (lane < a.R) masks[wave * K + a.E + lane] = mine;
     }
-    if (t < a.T) {
+    // tokens whose per-token outputs this block writes (all of them unless replicated)
+    const int tok_chunk = (ntile + nrep - 1) / nrep;
+    const bool my_token = t < a.T && tid >= replica * tok_chunk && tid < (replica + 1) * tok_chunk;
+    if (my_token) {
         // is_token_in_rank row: R bytes, written with the widest aligned stores
         uint8_t *out = a.itr + (size_t)t * a.R;
-        auto bytes4 = [&](int d) -> uint32_t {
-            const uint32_t x = (uint32_t)(rmask >> d) & 0xFu;
-            return (x & 1u) | ((x & 2u) << 7) | ((x & 4u) << 14) | ((x & 8u) << 21);
-        };
         if ((a.R & 15) == 0) {
             for (int d = 0; d < a.R; d += 16) {
-                const u32x4 v4 = {bytes4(d), bytes4(d + 4), bytes4(d + 8), bytes4(d + 12)};
+                const u32x4 v4 = {rank_bytes4(rmask, d), rank_bytes4(rmask, d + 4), rank_bytes4(rmask, d + 8),
+                                  rank_bytes4(rmask, d + 12)};
                 *reinterpret_cast<u32x4 *>(out + d) = v4;
             }
         } else if ((a.R & 7) == 0) {
             for (int d = 0; d < a.R; d += 8)
-                *reinterpret_cast<uint64_t *>(out + d) = (uint64_t)bytes4(d) | ((uint64_t)bytes4(d + 4) << 32);
+                *reinterpret_cast<uint64_t *>(out + d) =
+                    (uint64_t)rank_bytes4(rmask, d) | ((uint64_t)rank_bytes4(rmask, d + 4) << 32);
         } else if ((a.R & 3) == 0) {
-            for (int d = 0; d < a.R; d += 4) *reinterpret_cast<uint32_t *>(out + d) = bytes4(d);
+            for (int d = 0; d < a.R; d += 4) *reinterpret_cast<uint32_t *>(out + d) = rank_bytes4(rmask, d);
         } else {
             for (int d = 0; d < a.R; ++d) out[d] = (uint8_t)((rmask >> d) & 1);
         }
     }
-    if (st) atomicOr(&a.counters[kStatus], st);
+    if (st && replica == 0) atomicOr(&a.counters[kStatus], st);
     __syncthreads();
 
     // 2. per key: tokens in earlier waves and the tile's count; published at
     //    once for the look-back (tile 0's count is already its inclusive prefix)
     for (int key = tid; key < K; key += kTileTokens) {
-        int c = 0;
-#pragma unroll
-        for (int w = 0; w < kTileWaves; ++w) {
-            wpre[w * K + key] = c;
-            c += __popcll(masks[w * K + key]);
-        }
+        const int c0 = __popcll(masks[key]), c1 = __popcll(masks[K + key]), c2 = __popcll(masks[2 * K + key]),
+                  c3 = __popcll(masks[3 * K + key]);
+        wpre[key] = 0;
+        wpre[K + key] = c0;
+        wpre[2 * K + key] = c0 + c1;
+        wpre[3 * K + key] = c0 + c1 + c2;
+        const int c = c0 + c1 + c2 + c3;
         agg[key] = c;
         if (!single)
             __hip_atomic_store(a.tile_state + (size_t)tile * K + key,
@@ -275,39 +316,50 @@ __global__ __launch_bounds__(kTileTokens) void k_layout(LayoutArgs a) {
         }
         excl[key] = sum;
         const bool is_expert = key < a.E;
+        const KeyView kv = key_view(masks, K, key);
         if (single) {
-            // every boundary is here: per-source counts and offsets at once
-            int prev = 0;
-            for (int s = 0; s < a.R; ++s) {
-                const int nxt = count_before(masks, wpre, K, key, (s + 1) * a.tpr, ntile);
+            // every boundary is here: per-source counts and offsets at once,
+            // the replicas taking the source ranks in turn
+            for (int s = replica; s < a.R; s += nrep) {
+                const int lo = count_before(kv, s * a.tpr, ntile);
+                const int hi = count_before(kv, (s + 1) * a.tpr, ntile);
                 if (is_expert) {
-                    a.cnt_se[(size_t)s * a.E + key] = nxt - prev;
-                    a.src_expert_off[(size_t)s * a.E + key] = prev;
+                    a.cnt_se[(size_t)s * a.E + key] = hi - lo;
+                    a.src_expert_off[(size_t)s * a.E + key] = lo;
                 } else {
-                    a.cnt_sd[(size_t)s * a.R + (key - a.E)] = nxt - prev;
+                    a.cnt_sd[(size_t)s * a.R + (key - a.E)] = hi - lo;
                 }
-                prev = nxt;
             }
         } else {
-            for (int s = 0; s <= a.R; ++s) {
-                const int b = s * a.tpr;
-                if (boundary_owner(b, a.T, a.num_tiles) != tile) continue;
-                const int pre = sum + count_before(masks, wpre, K, key, b - t0, ntile);
-                a.bp[(size_t)s * K + key] = pre;
-                if (is_expert && s < a.R) a.src_expert_off[(size_t)s * a.E + key] = pre;
+            for (int s = first_lo; s < first_hi; ++s) {
+                const int pre = sum + count_before(kv, s * a.tpr - t0, ntile);
+                if (is_expert) a.src_expert_off[(size_t)s * a.E + key] = pre;
+                if (publish && s == first_hi - 1) a.bp[(size_t)s * K + key] = pre;
             }
         }
     }
     __syncthreads();
     if (!single && tid == 0) {
-        // this tile's boundary prefixes are visible to later tiles from here on
-        __threadfence();
-        __hip_atomic_store(a.bp_ready + tile, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (publish) {
+            // the start prefixes of the source that ends in a later tile are
+            // visible from here on
+            __threadfence();
+            __hip_atomic_store(a.bp_ready + tile, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if (last_tile) {
+            // The last tile's look-back has (transitively) seen every tile's
+            // published count, and a tile publishes only after reading the
+            // epoch: the workspace can be re-armed for the next call now.
+            uint32_t ne = (epoch + 1u) & ((1u << 30) - 1u);
+            if (ne == 0) ne = 1;
+            __hip_atomic_store(&a.counters[kTicket], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&a.counters[kEpoch], ne, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
 
     // 4. stable rank of each kept slot: tokens before it in earlier tiles,
     //    earlier waves of this tile, and earlier lanes of its wave
-    if (t < a.T) {
+    if (my_token) {
         const uint64_t below = bit - 1;
         int r[KMAX];
 #pragma unroll
@@ -330,17 +382,13 @@ __global__ __launch_bounds__(kTileTokens) void k_layout(LayoutArgs a) {
     // 5. per-source counts for the source ranks that end in this tile
     //    (source s = tokens [s*T/R, (s+1)*T/R)); a start boundary owned by an
     //    earlier tile is read back once that tile has published its prefixes
-    if (!single) {
-        int remote = -1;  // the one earlier tile whose boundary this tile may need
-        for (int s = 0; s < a.R; ++s) {
-            if (boundary_owner((s + 1) * a.tpr, a.T, a.num_tiles) != tile) continue;
-            const int o = boundary_owner(s * a.tpr, a.T, a.num_tiles);
-            if (o != tile) remote = o;
-        }
-        if (remote >= 0) {
+    if (!single && last_hi > last_lo) {
+        const bool remote = last_lo * a.tpr < t0;  // only the first such source can start earlier
+        if (remote) {
             if (tid == 0) {
+                const int owner = (last_lo * a.tpr) / kTileTokens;
                 uint32_t spins = 0;
-                while (__hip_atomic_load(a.bp_ready + remote, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != epoch) {
+                while (__hip_atomic_load(a.bp_ready + owner, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != epoch) {
                     if (++spins > a.spin_limit) {
                         atomicOr(&a.counters[kStatus], kStTimeout);
                         break;
@@ -351,16 +399,14 @@ __global__ __launch_bounds__(kTileTokens) void k_layout(LayoutArgs a) {
             }
             __syncthreads();
         }
-        for (int s = 0; s < a.R; ++s) {
-            const int bhi = (s + 1) * a.tpr;
-            if (boundary_owner(bhi, a.T, a.num_tiles) != tile) continue;
-            const int blo = s * a.tpr;
-            const bool local_lo = boundary_owner(blo, a.T, a.num_tiles) == tile;
-            for (int key = tid; key < K; key += kTileTokens) {
-                const int hi = excl[key] + count_before(masks, wpre, K, key, bhi - t0, ntile);
-                const int lo = local_lo ? excl[key] + count_before(masks, wpre, K, key, blo - t0, ntile)
-                                        : __hip_atomic_load(a.bp + (size_t)s * K + key, __ATOMIC_RELAXED,
-                                                            __HIP_MEMORY_SCOPE_AGENT);
+        for (int key = tid; key < K; key += kTileTokens) {
+            const KeyView kv = key_view(masks, K, key);
+            const int ex = excl[key];
+            for (int s = last_lo; s < last_hi; ++s) {
+                const int hi = ex + count_before(kv, (s + 1) * a.tpr - t0, ntile);
+                const int lo = s * a.tpr >= t0 ? ex + count_before(kv, s * a.tpr - t0, ntile)
+                                               : __hip_atomic_load(a.bp + (size_t)s * K + key, __ATOMIC_RELAXED,
+                                                                   __HIP_MEMORY_SCOPE_AGENT);
                 if (key < a.E)
                     a.cnt_se[(size_t)s * a.E + key] = hi - lo;
                 else
@@ -371,7 +417,7 @@ __global__ __launch_bounds__(kTileTokens) void k_layout(LayoutArgs a) {
 
     // 6. the last tile holds every key's total: rows per expert, expert
     //    offsets inside each rank (block scan), rows per rank
-    if (last_tile) {
+    if (last_tile && replica == 0) {
         __syncthreads();  // wpre is reused as the scan array below
         const int chunk = (a.E + kTileTokens - 1) / kTileTokens;
         const int lo = min(tid * chunk, a.E), hi = min(lo + chunk, a.E);
@@ -393,17 +439,6 @@ __global__ __launch_bounds__(kTileTokens) void k_layout(LayoutArgs a) {
             const int rows = scan[(d + 1) * a.epr] - scan[d * a.epr];
             a.rank_rows[d] = rows;
             if ((int64_t)rows > a.cap_rows) atomicOr(&a.counters[kStatus], kStCap);
-        }
-    }
-
-    // 7. the last tile to finish re-arms the workspace for the next call
-    if (!single && tid == 0) {
-        if (atomicAdd(&a.counters[kDone], 1u) == (unsigned)a.num_tiles - 1) {
-            uint32_t ne = (epoch + 1u) & ((1u << 30) - 1u);
-            if (ne == 0) ne = 1;
-            __hip_atomic_store(&a.counters[kTicket], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&a.counters[kDone], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&a.counters[kEpoch], ne, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 }
@@ -682,10 +717,12 @@ __global__ __launch_bounds__(256) void k_copy(const u32x4 *__restrict__ src, u32
 
 hipError_t launch_layout(const LayoutArgs &a, hipStream_t s) {
     const size_t lds = layout_lds_bytes(a.E + a.R);
+    // one tile: up to kLayoutReplicas copies, each writing a slice of the outputs
+    const int grid = a.num_tiles > 1 ? a.num_tiles : max(1, min(a.R, kLayoutReplicas));
     if (a.k <= 8)
-        hipLaunchKernelGGL(k_layout<8>, dim3(a.num_tiles), dim3(kTileTokens), lds, s, a);
+        hipLaunchKernelGGL(k_layout<8>, dim3(grid), dim3(kTileTokens), lds, s, a);
     else
-        hipLaunchKernelGGL(k_layout<kMaxTopk>, dim3(a.num_tiles), dim3(kTileTokens), lds, s, a);
+        hipLaunchKernelGGL(k_layout<kMaxTopk>, dim3(grid), dim3(kTileTokens), lds, s, a);
     return hipGetLastError();
 }
 
