@@ -36,7 +36,11 @@ def parse():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extras", action="store_true", help="skip decode/backward/copy extras")
+    p.add_argument("--no-decode", action="store_true", help="skip the decode-latency extra")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--record-traffic", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "TRACE_DIR"),
+                   help="summarize rocprofv3 runs of this bench (--pmc FETCH_SIZE, --pmc WRITE_SIZE, "
+                        "--kernel-trace --stats, all with --output-format csv) into profiles/")
     return p.parse_args()
 
 
@@ -160,18 +164,117 @@ def source_sha():
 
 
 def measured_traffic(kernel, workload):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if
-    it was taken on the current kernel sources (else None)."""
+    """HBM bytes per launch (calibrated FETCH_SIZE + WRITE_SIZE) from the
+    committed rocprofv3 counter summary, if it was taken on the current
+    kernel sources (else None)."""
     path = os.path.join(PROFILES, "traffic.json")
     try:
         with open(path) as f:
-            d = json.load(f)
-        e = d[workload][kernel]
-        if e.get("source_sha") != source_sha():
+            d = json.load(f)[workload]
+        if d.get("source_sha") != source_sha():
             return None
-        return e["hbm_bytes_per_launch"]
+        return d[kernel]["hbm_bytes_per_launch"]
     except (OSError, KeyError, ValueError):
         return None
+
+
+# ---------------------------------------------------------------------------
+# rocprofv3 summaries -> profiles/
+# ---------------------------------------------------------------------------
+
+KERNELS = {"k_layout": "k_layout", "k_dispatch": "k_dispatch<true, true>", "k_combine": "k_combine<false>",
+           "k_copy": "k_copy"}
+
+
+def _csv_rows(d, suffix):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True)
+    if not files:
+        raise SystemExit(f"no *{suffix} under {d}")
+    with open(files[0]) as f:
+        return list(csv.DictReader(f))
+
+
+def _per_kernel(rows, value_key):
+    """Dispatches per kernel of interest in launch order (the bench runs the
+    warmup and timed steps of the main loop first, so the first instances of
+    k_combine<false> are the forward combine, not dispatch_backward)."""
+    out = {k: [] for k in KERNELS}
+    for r in sorted(rows, key=lambda r: int(r.get("Dispatch_Id", r.get("Correlation_Id", 0)))):
+        for k, pat in KERNELS.items():
+            if pat in r["Kernel_Name"]:
+                out[k].append((int(r["Grid_Size"]), float(r[value_key])))
+    return out
+
+
+def record_traffic(args, cfg, nb_copy):
+    fetch = _per_kernel(_csv_rows(args.record_traffic[0], "counter_collection.csv"), "Counter_Value")
+    write = _per_kernel(_csv_rows(args.record_traffic[1], "counter_collection.csv"), "Counter_Value")
+    n = args.steps + args.warmup
+    mean = lambda xs: sum(xs) / len(xs)
+    # calibration: the copy kernel moves nb_copy bytes in and nb_copy out
+    f_copy = mean([v for g, v in fetch["k_copy"]]) * 1024.0
+    w_copy = mean([v for g, v in write["k_copy"]]) * 1024.0
+    f_scale, w_scale = nb_copy / f_copy, nb_copy / w_copy
+    res = {"source_sha": source_sha(), "workload": cfg.name,
+           "calibration": {"copy_bytes_each_way": nb_copy, "FETCH_SIZE_bytes": f_copy, "WRITE_SIZE_bytes": w_copy,
+                           "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)}}
+    for k in ("k_layout", "k_dispatch", "k_combine"):
+        # main-loop launches in order (the layout's first launch sizes the buffers)
+        first = 1 if k == "k_layout" else 0
+        fs = [v for g, v in fetch[k]][first:first + n]
+        ws = [v for g, v in write[k]][first:first + n]
+        fb, wb = mean(fs) * 1024.0 * f_scale, mean(ws) * 1024.0 * w_scale
+        res[k] = {"launches": len(fs), "fetch_bytes": round(fb), "write_bytes": round(wb),
+                  "hbm_bytes_per_launch": round(fb + wb)}
+    trace = _csv_rows(args.record_traffic[2], "kernel_stats.csv")
+    path = os.path.join(PROFILES, "traffic.json")
+    try:
+        with open(path) as f:
+            allres = json.load(f)
+    except (OSError, ValueError):
+        allres = {}
+    allres[cfg.name] = res
+    with open(path, "w") as f:
+        json.dump(allres, f, indent=1)
+    return res, trace
+
+
+def write_profile_summaries(args, cfg, res, trace, algo):
+    cmd_bench = f"python3 bench.py --config {cfg.name} --steps {args.steps} --warmup {args.warmup} --no-cpu-baseline --no-decode"
+    lines = [f"# {cfg.name}: kernel trace and HBM traffic (rocprofv3)", "",
+             f"Workload: {cfg.desc}.", "",
+             "Commands (run from /tmp with TMPDIR=/tmp; the bench runs from the repository root):", "",
+             f"    rocprofv3 --kernel-trace --stats --output-format csv -d <trace> -o run -- {cmd_bench}",
+             f"    rocprofv3 --pmc FETCH_SIZE --output-format csv -d <fetch> -o run -- {cmd_bench}",
+             f"    rocprofv3 --pmc WRITE_SIZE --output-format csv -d <write> -o run -- {cmd_bench}",
+             f"    python3 bench.py --config {cfg.name} --steps {args.steps} --warmup {args.warmup} "
+             "--record-traffic <fetch> <write> <trace>", "",
+             "## Kernel statistics (--kernel-trace --stats)", "",
+             "| kernel | calls | avg us | min us | max us | share % |", "|---|---|---|---|---|---|"]
+    for r in sorted(trace, key=lambda r: -float(r["TotalDurationNs"]))[:12]:
+        name = r["Name"].replace("ep::(anonymous namespace)::", "").replace("void ", "")
+        name = name.split("(")[0][:60]
+        lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f} |")
+    c = res["calibration"]
+    lines += ["", "## HBM traffic per launch (--pmc FETCH_SIZE, --pmc WRITE_SIZE)", "",
+              f"Calibration: the plain copy kernel moves {c['copy_bytes_each_way']} B each way; "
+              f"FETCH_SIZE reads {c['FETCH_SIZE_bytes']:.0f} B and WRITE_SIZE {c['WRITE_SIZE_bytes']:.0f} B "
+              f"for it, so the counters are scaled by {c['fetch_scale']} and {c['write_scale']}.", "",
+              "| kernel | launches | fetch MB | write MB | HBM MB | algorithmic MB | HBM / algorithmic |",
+              "|---|---|---|---|---|---|---|"]
+    for k in ("k_layout", "k_dispatch", "k_combine"):
+        e = res[k]
+        a = algo.get(k)
+        ratio = f"{e['hbm_bytes_per_launch'] / a:.3f}" if a else "-"
+        amb = f"{a / 1e6:.1f}" if a else "-"
+        lines.append(f"| `{k}` | {e['launches']} | {e['fetch_bytes'] / 1e6:.1f} | {e['write_bytes'] / 1e6:.1f} | "
+                     f"{e['hbm_bytes_per_launch'] / 1e6:.1f} | {amb} | {ratio} |")
+    lines += ["", f"Kernel sources: sha256 prefix {res['source_sha']} (ep_kernels.hip, ep_api.hip, ep_internal.h)."]
+    with open(os.path.join(PROFILES, f"{cfg.name}_kernels_and_traffic.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
 
 
 def cpu_baseline(path, seconds):
@@ -213,13 +316,23 @@ def main():
         print(f"bench.py: this build measures one GPU only (--gpus {args.gpus} requested); "
               "the multi-GPU exchange is not part of it.", file=sys.stderr)
         sys.exit(2)
-    import torch
-    from combine_get_dispatch_amd import ep, workloads
-    ep.load()
-    torch.cuda.set_device(0)
+    from combine_get_dispatch_amd import workloads
     cfg = workloads.CONFIGS[args.config]
     K, W = args.steps, args.warmup
+    if args.record_traffic:
+        # no GPU work: summarize the profiler output of an earlier run of this bench
+        wl = workloads.make_workload(cfg, seed=args.seed, with_x=False)
+        N = int((wl.topk_idx >= 0).sum())
+        d_b, c_b, _ = algo_bytes(cfg.T, cfg.k, cfg.H, N, cfg.use_fp8)
+        res, trace = record_traffic(args, cfg, (c_b // 2) // 16 * 16)
+        write_profile_summaries(args, cfg, res, trace, {"k_dispatch": d_b, "k_combine": c_b})
+        print(json.dumps(res))
+        return
 
+    import torch
+    from combine_get_dispatch_amd import ep
+    ep.load()
+    torch.cuda.set_device(0)
     main_path = Path(cfg, args.seed, torch, ep, workloads)
     ms, per_op = timed(torch, [main_path.layout_op, main_path.dispatch_op, main_path.combine_op], K, W)
     st = main_path.buf.status()
@@ -230,7 +343,7 @@ def main():
     value = (d_bytes + c_bytes) / (ms * 1e-3) / 1e9
     lay_ms, dis_ms, com_ms = per_op
     achieved = c_bytes / (com_ms * 1e-3) / 1e9
-    traffic = measured_traffic("combine", cfg.name)
+    traffic = measured_traffic("k_combine", cfg.name)
 
     out = {
         "metric": "dispatch+combine HBM GB/s & % of peak, 4096x7168 top-8; us at 128 tokens",
@@ -290,10 +403,12 @@ def main():
         out["copy_reference"] = {"bytes_moved": 2 * nb, "us": round(copy_ms * 1e3, 2),
                                  "GBps": round(2 * nb / (copy_ms * 1e-3) / 1e9, 1)}
         del src, dst
+    if not args.no_extras and not args.no_decode:
         # decode latency: 128 tokens (one rank's share) and the 8-rank group.
         # The step is launch-bound, so it is captured in a HIP graph and
         # replayed; eager per-op event times (host launch gaps included) are
         # reported beside it.
+        K = args.steps
         dec = {}
         for name in ("decode_rank", "decode"):
             dp = Path(workloads.CONFIGS[name], args.seed, torch, ep, workloads)
