@@ -38,6 +38,9 @@ def parse():
     p.add_argument("--no-extras", action="store_true", help="skip decode/backward/copy extras")
     p.add_argument("--no-decode", action="store_true", help="skip the decode-latency extra")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--separate", action="store_true",
+                   help="time the step as three calls (layout, dispatch, combine) instead of the fused "
+                        "layout+dispatch launch followed by combine")
     p.add_argument("--record-traffic", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "TRACE_DIR"),
                    help="summarize rocprofv3 runs of this bench (--pmc FETCH_SIZE, --pmc WRITE_SIZE, "
                         "--kernel-trace --stats, all with --output-format csv) into profiles/")
@@ -95,6 +98,10 @@ class Path:
     def dispatch_op(self):
         self.buf.dispatch(self.x, self.topk, self.w, self.layout, self.cfg.use_fp8,
                           out=(self.recv_x, self.recv_scales, self.recv_w, self.handle))
+
+    def fused_op(self):
+        self.buf.dispatch_with_layout(self.x, self.topk, self.w, self.cfg.use_fp8, layout=self.layout,
+                                      out=(self.recv_x, self.recv_scales, self.recv_w, self.handle))
 
     def combine_op(self):
         self.buf.combine(self.expert_out, self.handle, self.w, out=self.y)
@@ -182,8 +189,8 @@ def measured_traffic(kernel, workload):
 # rocprofv3 summaries -> profiles/
 # ---------------------------------------------------------------------------
 
-KERNELS = {"k_layout": "k_layout", "k_dispatch": "k_dispatch<true, true>", "k_combine": "k_combine<false>",
-           "k_copy": "k_copy"}
+KERNELS = {"k_layout": "k_layout<", "k_layout_dispatch": "k_layout_dispatch<", "k_dispatch": "k_dispatch<true, true>",
+           "k_combine": "k_combine<false>", "k_copy": "k_copy"}
 
 
 def _csv_rows(d, suffix):
@@ -220,7 +227,7 @@ def record_traffic(args, cfg, nb_copy):
     res = {"source_sha": source_sha(), "workload": cfg.name,
            "calibration": {"copy_bytes_each_way": nb_copy, "FETCH_SIZE_bytes": f_copy, "WRITE_SIZE_bytes": w_copy,
                            "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)}}
-    for k in ("k_layout", "k_dispatch", "k_combine"):
+    for k in ("k_layout_dispatch", "k_layout", "k_dispatch", "k_combine"):
         # main-loop launches in order (the layout's first launch sizes the buffers)
         first = 1 if k == "k_layout" else 0
         fs = [v for g, v in fetch[k]][first:first + n]
@@ -265,7 +272,7 @@ def write_profile_summaries(args, cfg, res, trace, algo):
               f"for it, so the counters are scaled by {c['fetch_scale']} and {c['write_scale']}.", "",
               "| kernel | launches | fetch MB | write MB | HBM MB | algorithmic MB | HBM / algorithmic |",
               "|---|---|---|---|---|---|---|"]
-    for k in ("k_layout", "k_dispatch", "k_combine"):
+    for k in ("k_layout_dispatch", "k_layout", "k_dispatch", "k_combine"):
         e = res[k]
         a = algo.get(k)
         ratio = f"{e['hbm_bytes_per_launch'] / a:.3f}" if a else "-"
@@ -325,7 +332,7 @@ def main():
         N = int((wl.topk_idx >= 0).sum())
         d_b, c_b, _ = algo_bytes(cfg.T, cfg.k, cfg.H, N, cfg.use_fp8)
         res, trace = record_traffic(args, cfg, (c_b // 2) // 16 * 16)
-        write_profile_summaries(args, cfg, res, trace, {"k_dispatch": d_b, "k_combine": c_b})
+        write_profile_summaries(args, cfg, res, trace, {"k_layout_dispatch": d_b, "k_dispatch": d_b, "k_combine": c_b})
         print(json.dumps(res))
         return
 
@@ -334,14 +341,18 @@ def main():
     ep.load()
     torch.cuda.set_device(0)
     main_path = Path(cfg, args.seed, torch, ep, workloads)
-    ms, per_op = timed(torch, [main_path.layout_op, main_path.dispatch_op, main_path.combine_op], K, W)
+    fused = not args.separate
+    if fused:
+        ms, (ld_ms, com_ms) = timed(torch, [main_path.fused_op, main_path.combine_op], K, W)
+    else:
+        ms, (lay_ms, dis_ms, com_ms) = timed(torch, [main_path.layout_op, main_path.dispatch_op,
+                                                     main_path.combine_op], K, W)
     st = main_path.buf.status()
     if st:
         raise SystemExit(f"bench: device status {st} on {cfg.name}")
     N = main_path.kept_slots()
     d_bytes, c_bytes, cb_bytes = algo_bytes(cfg.T, cfg.k, cfg.H, N, cfg.use_fp8)
     value = (d_bytes + c_bytes) / (ms * 1e-3) / 1e9
-    lay_ms, dis_ms, com_ms = per_op
     achieved = c_bytes / (com_ms * 1e-3) / 1e9
     traffic = measured_traffic("k_combine", cfg.name)
 
@@ -361,21 +372,38 @@ def main():
         "config": {"workload": cfg.name, "tokens": cfg.T, "hidden": cfg.H, "experts": cfg.E,
                    "ranks_simulated": cfg.R, "topk": cfg.k, "routing": cfg.routing,
                    "fp8_dispatch": cfg.use_fp8, "cap_rows": main_path.cap, "kept_slots": N,
-                   "step": "layout + dispatch + combine"},
+                   "step": "fused layout+dispatch launch, then combine" if fused
+                   else "layout, dispatch, combine (three launches)"},
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "kernel": "k_combine", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": c_bytes},
-        "kernels": {
-            "layout": {"us": round(lay_ms * 1e3, 2)},
-            "dispatch": {"us": round(dis_ms * 1e3, 2), "bytes": d_bytes,
-                         "GBps": round(d_bytes / (dis_ms * 1e-3) / 1e9, 1)},
-            "combine": {"us": round(com_ms * 1e3, 2), "bytes": c_bytes,
-                        "GBps": round(achieved, 1)},
-        },
+        "kernels": {},
     }
-    print(f"# main: {ms * 1e3:.1f} us/step  layout {lay_ms * 1e3:.1f}  dispatch {dis_ms * 1e3:.1f}  "
-          f"combine {com_ms * 1e3:.1f} us", file=sys.stderr, flush=True)
+    if fused:
+        out["kernels"]["layout_dispatch"] = {"us": round(ld_ms * 1e3, 2), "bytes": d_bytes,
+                                             "GBps": round(d_bytes / (ld_ms * 1e-3) / 1e9, 1)}
+    else:
+        out["kernels"]["layout"] = {"us": round(lay_ms * 1e3, 2)}
+        out["kernels"]["dispatch"] = {"us": round(dis_ms * 1e3, 2), "bytes": d_bytes,
+                                      "GBps": round(d_bytes / (dis_ms * 1e-3) / 1e9, 1)}
+    out["kernels"]["combine"] = {"us": round(com_ms * 1e3, 2), "bytes": c_bytes, "GBps": round(achieved, 1)}
+    print(f"# main: {ms * 1e3:.1f} us/step  " +
+          "  ".join(f"{k} {v['us']:.1f}" for k, v in out["kernels"].items()) + " us", file=sys.stderr, flush=True)
+
+    if not args.no_extras:
+        # the other form of the same step, on the same buffers
+        p = main_path
+        if fused:
+            ams, (l_, d_, c_) = timed(torch, [p.layout_op, p.dispatch_op, p.combine_op], K, W)
+            out["separate_calls"] = {"us_per_step": round(ams * 1e3, 2), "layout_us": round(l_ * 1e3, 2),
+                                     "dispatch_us": round(d_ * 1e3, 2), "combine_us": round(c_ * 1e3, 2)}
+        else:
+            ams, (ld_, c_) = timed(torch, [p.fused_op, p.combine_op], K, W)
+            out["fused_launch"] = {"us_per_step": round(ams * 1e3, 2), "layout_dispatch_us": round(ld_ * 1e3, 2),
+                                   "combine_us": round(c_ * 1e3, 2)}
+        if p.buf.status():
+            raise SystemExit(f"bench: device status {p.buf.status()} on {cfg.name}")
 
     if not args.no_extras:
         # backward pair on the same handle (bf16 gradients)
@@ -412,16 +440,19 @@ def main():
         dec = {}
         for name in ("decode_rank", "decode"):
             dp = Path(workloads.CONFIGS[name], args.seed, torch, ep, workloads)
-            ops = [dp.layout_op, dp.dispatch_op, dp.combine_op]
-            g_us, g_wall = graph_timed(torch, ops, max(K, 200), W)
-            dms, (l_, d_, c_) = timed(torch, ops, max(K, 100), W)
+            ops3 = [dp.layout_op, dp.dispatch_op, dp.combine_op]
+            ops2 = [dp.fused_op, dp.combine_op]
+            g_us, g_wall = graph_timed(torch, ops2 if fused else ops3, max(K, 200), W)
+            g3_us, _ = graph_timed(torch, ops3, max(K, 200), W)
+            dms, (ld_, c_) = timed(torch, ops2, max(K, 100), W)
             dst_ = dp.buf.status()
             dd, dc, _ = algo_bytes(dp.cfg.T, dp.cfg.k, dp.cfg.H, dp.kept_slots(), True)
             dec[name] = {"tokens": dp.cfg.T, "us_per_step_graph": round(g_us, 2),
                          "us_per_step_graph_wall": round(g_wall, 2),
                          "GBps_graph": round((dd + dc) / (g_us * 1e-6) / 1e9, 1),
+                         "us_per_step_graph_three_launches": round(g3_us, 2),
                          "us_per_step_eager": round(dms * 1e3, 2),
-                         "eager_layout_us": round(l_ * 1e3, 2), "eager_dispatch_us": round(d_ * 1e3, 2),
+                         "eager_layout_dispatch_us": round(ld_ * 1e3, 2),
                          "eager_combine_us": round(c_ * 1e3, 2), "status": dst_}
             dp.buf.close()
             del dp

@@ -20,6 +20,7 @@ struct ep_ctx {
     uint64_t *tile_state;
     int32_t *bp;
     uint32_t *bp_ready;
+    uint32_t *rank_ready;
     uint32_t spin_limit;
     bool debug;
 };
@@ -56,17 +57,28 @@ int num_tiles_of(const ep_config &c) {
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// workspace: counters | tile states | boundary prefixes | boundary-ready flags
-size_t workspace_layout(const ep_config &c, size_t *off_state, size_t *off_bp, size_t *off_ready) {
+// workspace: counters | tile states | boundary prefixes | boundary-ready
+// flags | rank-ready flags (one per layout block of a fused launch)
+struct WorkspaceLayout {
+    size_t state, bp, bp_ready, rank_ready, total;
+};
+
+WorkspaceLayout workspace_layout(const ep_config &c) {
     const size_t keys = (size_t)c.num_experts + c.num_ranks;
+    const size_t tiles = (size_t)num_tiles_of(c);
+    const size_t blocks = tiles > (size_t)ep::kLayoutReplicas ? tiles : (size_t)ep::kLayoutReplicas;
+    WorkspaceLayout w;
     size_t off = round_up(ep::kNumCounters * sizeof(uint32_t), 256);
-    *off_state = off;
-    off = round_up(off + (size_t)num_tiles_of(c) * keys * sizeof(uint64_t), 256);
-    *off_bp = off;
+    w.state = off;
+    off = round_up(off + tiles * keys * sizeof(uint64_t), 256);
+    w.bp = off;
     off = round_up(off + ((size_t)c.num_ranks + 1) * keys * sizeof(int32_t), 256);
-    *off_ready = off;
-    off = round_up(off + (size_t)num_tiles_of(c) * sizeof(uint32_t), 256);
-    return off;
+    w.bp_ready = off;
+    off = round_up(off + tiles * sizeof(uint32_t), 256);
+    w.rank_ready = off;
+    off = round_up(off + blocks * sizeof(uint32_t), 256);
+    w.total = off;
+    return w;
 }
 
 // Work split of a token-major kernel: waves_per_token waves share a token's
@@ -129,15 +141,21 @@ int combine_common(ep_ctx *ctx, const uint16_t *rows, const ep_handle *h, const 
     return hip_fail(ep::launch_combine(a, out_f32, g.num_waves, (hipStream_t)stream), name);
 }
 
-int dispatch_common(ep_ctx *ctx, const uint16_t *x, const int32_t *topk, const float *w, const ep_layout *L,
-                    bool fp8, bool forward, void *recv_x, float *recv_scales, float *recv_w, ep_handle *h,
-                    ep_stream_t stream, const char *name) {
+// log2(v) when v is a power of two, else -1
+int log2_exact(int v) {
+    if (v <= 0 || (v & (v - 1))) return -1;
+    int s = 0;
+    while ((1 << s) < v) ++s;
+    return s;
+}
+
+int fill_dispatch(ep_ctx *ctx, const uint16_t *x, const int32_t *topk, const float *w, const ep_layout *L,
+                  bool forward, void *recv_x, float *recv_scales, float *recv_w, ep_handle *h, ep::DispatchArgs &a,
+                  Geometry &g) {
     const ep_config &c = ctx->cfg;
-    if (c.num_tokens == 0) return EP_OK;
     if (!x || (!recv_x && c.cap_rows > 0)) return EP_ERR_ARG;
     if (!aligned(x, 16) || !aligned(recv_x, 16) || !aligned(h->pos, 4)) return EP_ERR_ALIGN;
-    const Geometry g = geometry(c.num_tokens, c.hidden, kDispatchTargetWaves);
-    ep::DispatchArgs a;
+    g = geometry(c.num_tokens, c.hidden, kDispatchTargetWaves);
     std::memset(&a, 0, sizeof a);
     a.x = x;
     a.topk = topk;
@@ -155,6 +173,7 @@ int dispatch_common(ep_ctx *ctx, const uint16_t *x, const int32_t *topk, const f
     a.k = c.num_topk;
     a.E = c.num_experts;
     a.epr = c.num_experts / c.num_ranks;
+    a.epr_shift = log2_exact(a.epr);
     a.H = c.hidden;
     a.cap_rows = c.cap_rows;
     a.num_rows = (int64_t)c.num_ranks * c.cap_rows;
@@ -162,10 +181,80 @@ int dispatch_common(ep_ctx *ctx, const uint16_t *x, const int32_t *topk, const f
     a.passes_per_wave = g.ppw;
     a.npass = g.npass;
     a.counters = ctx->counters;
+    return EP_OK;
+}
+
+int dispatch_common(ep_ctx *ctx, const uint16_t *x, const int32_t *topk, const float *w, const ep_layout *L,
+                    bool fp8, bool forward, void *recv_x, float *recv_scales, float *recv_w, ep_handle *h,
+                    ep_stream_t stream, const char *name) {
+    const ep_config &c = ctx->cfg;
+    if (c.num_tokens == 0) return EP_OK;
+    ep::DispatchArgs a;
+    Geometry g;
+    if (int r = fill_dispatch(ctx, x, topk, w, L, forward, recv_x, recv_scales, recv_w, h, a, g)) return r;
     if (ctx->debug)
         std::fprintf(stderr, "libep: %s T=%d k=%d H=%d fp8=%d waves=%d (%d/token, %d passes each)\n", name,
                      a.T, a.k, a.H, (int)fp8, g.num_waves, g.wpt, g.ppw);
     return hip_fail(ep::launch_dispatch(a, fp8, forward, g.num_waves, (hipStream_t)stream), name);
+}
+
+int fill_layout(ep_ctx *ctx, const int32_t *topk_idx, const ep_layout *L, ep::LayoutArgs &a) {
+    if (!ctx || !L) return EP_ERR_ARG;
+    const ep_config &c = ctx->cfg;
+    if (!L->cnt_se || !L->cnt_sd || !L->recv_cnt || !L->expert_off || !L->rank_rows || !L->src_expert_off)
+        return EP_ERR_ARG;
+    if (c.num_tokens > 0 && (!topk_idx || !L->rank_in_expert || !L->is_token_in_rank)) return EP_ERR_ARG;
+    if (!aligned(topk_idx, 4) || !aligned(L->rank_in_expert, 16) || !aligned(L->is_token_in_rank, 16) ||
+        !aligned(L->cnt_se, 4) || !aligned(L->cnt_sd, 4) || !aligned(L->recv_cnt, 4) ||
+        !aligned(L->expert_off, 4) || !aligned(L->rank_rows, 4) || !aligned(L->src_expert_off, 4))
+        return EP_ERR_ALIGN;
+    std::memset(&a, 0, sizeof a);
+    // the slot loads read a clamped row even with no tokens: then they read
+    // the workspace (at least kMaxTopk ints) instead of a possibly null array
+    a.topk = c.num_tokens > 0 ? topk_idx : reinterpret_cast<const int32_t *>(ctx->ws);
+    a.T = c.num_tokens;
+    a.k = c.num_topk;
+    a.E = c.num_experts;
+    a.R = c.num_ranks;
+    a.epr = c.num_experts / c.num_ranks;
+    a.epr_shift = log2_exact(a.epr);
+    a.tpr = c.num_tokens / c.num_ranks;
+    a.num_tiles = ctx->num_tiles;
+    a.use_ticket = ctx->num_tiles > ep::kCoResidentTiles;
+    a.cap_rows = c.cap_rows;
+    a.rank_in_expert = L->rank_in_expert;
+    a.itr = L->is_token_in_rank;
+    a.cnt_se = L->cnt_se;
+    a.cnt_sd = L->cnt_sd;
+    a.recv_cnt = L->recv_cnt;
+    a.expert_off = L->expert_off;
+    a.rank_rows = L->rank_rows;
+    a.src_expert_off = L->src_expert_off;
+    a.tile_state = ctx->tile_state;
+    a.bp = ctx->bp;
+    a.bp_ready = ctx->bp_ready;
+    a.rank_ready = ctx->rank_ready;
+    a.counters = ctx->counters;
+    a.spin_limit = ctx->spin_limit;
+    return EP_OK;
+}
+
+// Shared checks of the forward dispatch arguments; sets the handle's config.
+int check_forward_dispatch(ep_ctx *ctx, const int32_t *topk_idx, const float *topk_weights, const ep_layout *L,
+                           int use_fp8, float *recv_scales, float *recv_w, ep_handle *handle) {
+    if (!ctx || !L || !handle) return EP_ERR_ARG;
+    const ep_config &c = ctx->cfg;
+    if (use_fp8 != 0 && use_fp8 != 1) return EP_ERR_ARG;
+    if (use_fp8 && (c.hidden % 128 || (!recv_scales && c.cap_rows > 0))) return EP_ERR_ARG;
+    if (!use_fp8 && recv_scales) return EP_ERR_ARG;
+    if ((!handle->pos && c.num_tokens > 0) || (!handle->src_idx && c.cap_rows > 0)) return EP_ERR_ARG;
+    if (c.num_tokens > 0 && (!topk_idx || !L->rank_in_expert || !L->expert_off)) return EP_ERR_ARG;
+    if (!aligned(topk_idx, 4) || !aligned(topk_weights, 4) || !aligned(recv_w, 4) || !aligned(recv_scales, 4) ||
+        !aligned(handle->src_idx, 4))
+        return EP_ERR_ALIGN;
+    handle->num_tokens = c.num_tokens;
+    handle->num_topk = c.num_topk;
+    return EP_OK;
 }
 
 }  // namespace
@@ -206,8 +295,7 @@ int ep_query_sizes(const ep_config *cfg, ep_sizes *out) {
     out->recv_scales = rows * (H / 128) * 4;
     out->recv_w = rows * 4;
     out->combined_x = T * H * 2;
-    size_t a, b, r;
-    out->workspace = workspace_layout(*cfg, &a, &b, &r);
+    out->workspace = workspace_layout(*cfg).total;
     return EP_OK;
 }
 
@@ -220,8 +308,8 @@ int ep_create(const ep_config *cfg, ep_ctx **out) {
     ctx->cfg = *cfg;
     ctx->num_tiles = num_tiles_of(*cfg);
     ctx->keys = cfg->num_experts + cfg->num_ranks;
-    size_t off_state, off_bp, off_ready;
-    ctx->ws_bytes = workspace_layout(*cfg, &off_state, &off_bp, &off_ready);
+    const WorkspaceLayout wl = workspace_layout(*cfg);
+    ctx->ws_bytes = wl.total;
     const char *dbg = std::getenv("EP_DEBUG");
     ctx->debug = dbg && dbg[0] && dbg[0] != '0';
     const char *spin = std::getenv("EP_SPIN_LIMIT");
@@ -236,9 +324,10 @@ int ep_create(const ep_config *cfg, ep_ctx **out) {
     }
     char *base = static_cast<char *>(ctx->ws);
     ctx->counters = reinterpret_cast<uint32_t *>(base);
-    ctx->tile_state = reinterpret_cast<uint64_t *>(base + off_state);
-    ctx->bp = reinterpret_cast<int32_t *>(base + off_bp);
-    ctx->bp_ready = reinterpret_cast<uint32_t *>(base + off_ready);
+    ctx->tile_state = reinterpret_cast<uint64_t *>(base + wl.state);
+    ctx->bp = reinterpret_cast<int32_t *>(base + wl.bp);
+    ctx->bp_ready = reinterpret_cast<uint32_t *>(base + wl.bp_ready);
+    ctx->rank_ready = reinterpret_cast<uint32_t *>(base + wl.rank_ready);
     uint32_t init[ep::kNumCounters] = {0};
     init[ep::kEpoch] = 1;  // tile states start at epoch 0 = "not published"
     int r = hip_fail(hipMemset(ctx->ws, 0, ctx->ws_bytes), "hipMemset");
@@ -266,39 +355,8 @@ int ep_destroy(ep_ctx *ctx) {
 }
 
 int ep_get_dispatch_layout(ep_ctx *ctx, const int32_t *topk_idx, const ep_layout *L, ep_stream_t stream) {
-    if (!ctx || !L) return EP_ERR_ARG;
-    const ep_config &c = ctx->cfg;
-    if (!L->cnt_se || !L->cnt_sd || !L->recv_cnt || !L->expert_off || !L->rank_rows || !L->src_expert_off)
-        return EP_ERR_ARG;
-    if (c.num_tokens > 0 && (!topk_idx || !L->rank_in_expert || !L->is_token_in_rank)) return EP_ERR_ARG;
-    if (!aligned(topk_idx, 4) || !aligned(L->rank_in_expert, 16) || !aligned(L->is_token_in_rank, 16) ||
-        !aligned(L->cnt_se, 4) || !aligned(L->cnt_sd, 4) || !aligned(L->recv_cnt, 4) ||
-        !aligned(L->expert_off, 4) || !aligned(L->rank_rows, 4) || !aligned(L->src_expert_off, 4))
-        return EP_ERR_ALIGN;
     ep::LayoutArgs a;
-    a.topk = topk_idx;
-    a.T = c.num_tokens;
-    a.k = c.num_topk;
-    a.E = c.num_experts;
-    a.R = c.num_ranks;
-    a.epr = c.num_experts / c.num_ranks;
-    a.tpr = c.num_tokens / c.num_ranks;
-    a.num_tiles = ctx->num_tiles;
-    a.use_ticket = ctx->num_tiles > ep::kCoResidentTiles;
-    a.cap_rows = c.cap_rows;
-    a.rank_in_expert = L->rank_in_expert;
-    a.itr = L->is_token_in_rank;
-    a.cnt_se = L->cnt_se;
-    a.cnt_sd = L->cnt_sd;
-    a.recv_cnt = L->recv_cnt;
-    a.expert_off = L->expert_off;
-    a.rank_rows = L->rank_rows;
-    a.src_expert_off = L->src_expert_off;
-    a.tile_state = ctx->tile_state;
-    a.bp = ctx->bp;
-    a.bp_ready = ctx->bp_ready;
-    a.counters = ctx->counters;
-    a.spin_limit = ctx->spin_limit;
+    if (int r = fill_layout(ctx, topk_idx, L, a)) return r;
     if (ctx->debug)
         std::fprintf(stderr, "libep: layout T=%d k=%d E=%d R=%d tiles=%d\n", a.T, a.k, a.E, a.R, a.num_tiles);
     return hip_fail(ep::launch_layout(a, (hipStream_t)stream), "ep_get_dispatch_layout");
@@ -307,20 +365,37 @@ int ep_get_dispatch_layout(ep_ctx *ctx, const int32_t *topk_idx, const ep_layout
 int ep_dispatch(ep_ctx *ctx, const uint16_t *x, const int32_t *topk_idx, const float *topk_weights,
                 const ep_layout *L, int use_fp8, void *recv_x, float *recv_scales, float *recv_w,
                 ep_handle *handle, ep_stream_t stream) {
-    if (!ctx || !L || !handle) return EP_ERR_ARG;
-    const ep_config &c = ctx->cfg;
-    if (use_fp8 != 0 && use_fp8 != 1) return EP_ERR_ARG;
-    if (use_fp8 && (c.hidden % 128 || (!recv_scales && c.cap_rows > 0))) return EP_ERR_ARG;
-    if (!use_fp8 && recv_scales) return EP_ERR_ARG;
-    if ((!handle->pos && c.num_tokens > 0) || (!handle->src_idx && c.cap_rows > 0)) return EP_ERR_ARG;
-    if (c.num_tokens > 0 && (!topk_idx || !L->rank_in_expert || !L->expert_off)) return EP_ERR_ARG;
-    if (!aligned(topk_idx, 4) || !aligned(topk_weights, 4) || !aligned(recv_w, 4) || !aligned(recv_scales, 4) ||
-        !aligned(handle->src_idx, 4))
-        return EP_ERR_ALIGN;
-    handle->num_tokens = c.num_tokens;
-    handle->num_topk = c.num_topk;
+    if (int r = check_forward_dispatch(ctx, topk_idx, topk_weights, L, use_fp8, recv_scales, recv_w, handle))
+        return r;
     return dispatch_common(ctx, x, topk_idx, topk_weights, L, use_fp8 != 0, true, recv_x, recv_scales, recv_w,
                            handle, stream, "ep_dispatch");
+}
+
+int ep_dispatch_with_layout(ep_ctx *ctx, const uint16_t *x, const int32_t *topk_idx, const float *topk_weights,
+                            const ep_layout *L, int use_fp8, void *recv_x, float *recv_scales, float *recv_w,
+                            ep_handle *handle, ep_stream_t stream) {
+    ep::LayoutArgs la;
+    if (int r = fill_layout(ctx, topk_idx, L, la)) return r;
+    if (int r = check_forward_dispatch(ctx, topk_idx, topk_weights, L, use_fp8, recv_scales, recv_w, handle))
+        return r;
+    const ep_config &c = ctx->cfg;
+    if (c.num_tokens == 0)  // nothing to pack: the layout alone (zero counts)
+        return hip_fail(ep::launch_layout(la, (hipStream_t)stream), "ep_dispatch_with_layout");
+    ep::DispatchArgs da;
+    Geometry g;
+    if (int r = fill_dispatch(ctx, x, topk_idx, topk_weights, L, true, recv_x, recv_scales, recv_w, handle, da, g))
+        return r;
+    if (ctx->debug)
+        std::fprintf(stderr, "libep: layout+dispatch T=%d k=%d E=%d R=%d H=%d fp8=%d tiles=%d waves=%d\n", c.num_tokens,
+                     c.num_topk, c.num_experts, c.num_ranks, c.hidden, use_fp8, ctx->num_tiles, g.num_waves);
+    // One tile: every dispatch block builds the layout itself (no waits).
+    // Otherwise the layout blocks raise flags the dispatch blocks wait on.
+    const int keys = c.num_experts + c.num_ranks;
+    if (ctx->num_tiles == 1 && ep::inblock_lds_bytes(keys, c.num_topk) <= ep::kMaxBlockLds)
+        return hip_fail(ep::launch_dispatch_inblock(la, da, use_fp8 != 0, g.num_waves, (hipStream_t)stream),
+                        "ep_dispatch_with_layout");
+    return hip_fail(ep::launch_layout_dispatch(la, da, use_fp8 != 0, g.num_waves, (hipStream_t)stream),
+                    "ep_dispatch_with_layout");
 }
 
 int ep_combine(ep_ctx *ctx, const uint16_t *expert_out, const ep_handle *handle, const float *weights,

@@ -15,16 +15,21 @@ constexpr int kLayoutTile = 256;
 constexpr int kCoResidentTiles = 256;  // grids up to this size number tiles by block index
 constexpr int kLayoutReplicas = 8;     // blocks sharing the outputs of a single tile
 inline size_t layout_lds_bytes(int keys) { return (size_t)keys * (4 * 8 + 4 * 4 + 2 * 4); }
+// A fused launch on a single tile: every dispatch block builds the whole
+// layout in its own LDS and keeps each slot's (expert, rank) beside it.
+inline size_t inblock_lds_bytes(int keys, int k) { return layout_lds_bytes(keys) + (size_t)kLayoutTile * k * 4; }
+constexpr size_t kMaxBlockLds = 64 * 1024;
 constexpr int kMaxTopk = 32;
 constexpr int kMaxRanks = 64;
 constexpr int kMaxExperts = 1024;
 
 // ctx workspace counters (uint32 each)
-enum Counter { kTicket = 0, kEpoch = 2, kStatus = 3, kNumCounters = 16 };
+enum Counter { kTicket = 0, kDone = 1, kEpoch = 2, kStatus = 3, kTotalsReady = 4, kNumCounters = 16 };
 
 struct LayoutArgs {
     const int32_t *topk;
     int T, k, E, R, epr, tpr, num_tiles;
+    int epr_shift;   // log2(epr) when epr is a power of two, else -1
     int use_ticket;  // number tiles by start order (large grids) instead of block index
     int64_t cap_rows;
     int32_t *rank_in_expert;
@@ -33,6 +38,7 @@ struct LayoutArgs {
     uint64_t *tile_state;  // [num_tiles][E+R]
     int32_t *bp;           // [R+1][E+R] prefixes at source-rank boundaries
     uint32_t *bp_ready;    // [num_tiles] epoch once a tile's boundary prefixes are written
+    uint32_t *rank_ready;  // [layout blocks] epoch once a block's ranks are written (fused launch)
     uint32_t *counters;
     uint32_t spin_limit;
 };
@@ -48,7 +54,7 @@ struct DispatchArgs {
     float *recv_w;               // [R*cap] or NULL (forward only)
     void *recv_x;                // [R*cap][H] e4m3 or bf16
     float *recv_scales;          // [R*cap][H/128] (FP8 only)
-    int T, k, E, epr, H;
+    int T, k, E, epr, epr_shift, H;
     int64_t cap_rows, num_rows;  // num_rows = R * cap_rows
     int waves_per_token, passes_per_wave, npass;
     uint32_t *counters;
@@ -68,6 +74,10 @@ struct CombineArgs {
 hipError_t launch_layout(const LayoutArgs &a, hipStream_t s);
 hipError_t launch_dispatch(const DispatchArgs &a, bool fp8, bool forward, int num_waves,
                            hipStream_t s);
+hipError_t launch_dispatch_inblock(const LayoutArgs &la, const DispatchArgs &da, bool fp8, int num_waves,
+                                   hipStream_t s);
+hipError_t launch_layout_dispatch(const LayoutArgs &la, const DispatchArgs &da, bool fp8, int num_waves,
+                                  hipStream_t s);
 hipError_t launch_combine(const CombineArgs &a, bool out_f32, int num_waves, hipStream_t s);
 hipError_t launch_copy(const void *src, void *dst, size_t n16, hipStream_t s);
 

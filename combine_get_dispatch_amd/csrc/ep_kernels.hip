@@ -70,8 +70,9 @@ constexpr int kLookbackWindow = 32;  // predecessor states read per round trip
 constexpr int kTileWaves = 4;
 constexpr int kTileTokens = kTileWaves * 64;
 
-// Exclusive prefix sum of one int per thread over the block (wave scan with
-// lane shuffles, then the wave totals). *total receives the block sum.
+// Exclusive prefix sum of one int per thread over a block of NW waves (wave
+// scan with lane shuffles, then the wave totals). *total receives the sum.
+template <int NW = kTileWaves>
 __device__ __forceinline__ int block_exclusive_scan(int v, int *s_part, int *total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     int x = v;
@@ -84,15 +85,15 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int *s_part, int *tot
     __syncthreads();
     if (threadIdx.x == 0) {
         int run = 0;
-        for (int w = 0; w < kTileWaves; ++w) {
+        for (int w = 0; w < NW; ++w) {
             const int c = s_part[w];
             s_part[w] = run;
             run += c;
         }
-        s_part[kTileWaves] = run;
+        s_part[NW] = run;
     }
     __syncthreads();
-    *total = s_part[kTileWaves];
+    *total = s_part[NW];
     return s_part[wave] + x - v;
 }
 
@@ -129,37 +130,73 @@ __device__ __forceinline__ uint32_t rank_bytes4(uint64_t rmask, int d) {
     return (x & 1u) | ((x & 2u) << 7) | ((x & 4u) << 14) | ((x & 8u) << 21);
 }
 
-template <int KMAX>
-__global__ __launch_bounds__(kTileTokens) void k_layout(LayoutArgs a) {
+// How a layout block runs: alone (its own grid), in a fused grid whose
+// dispatch blocks wait on its readiness flags, or inside every dispatch block
+// of a single-tile fused grid (the block keeps the whole layout in its LDS).
+enum LayoutMode { kLayoutAlone = 0, kLayoutFlags = 1, kLayoutInBlock = 2 };
+
+// Expert e's rank: a shift when the experts per rank are a power of two.
+__device__ __forceinline__ int rank_of(int e, int epr, int shift) { return shift >= 0 ? e >> shift : e / epr; }
+
+// The layout's LDS, carved from the dynamic allocation (K = E + R keys).
+struct LayoutLds {
+    uint64_t *masks;  // [4 waves][K] token bitmasks per wave
+    int32_t *wpre;    // [4][K] tokens in earlier waves
+    int32_t *excl;    // [K] tokens in earlier tiles
+    int32_t *agg;     // [K] tokens in this tile
+    int32_t *scan;    // last step only (aliases wpre): [E+1] prefix of expert rows
+    int32_t *slots;   // in-block mode: [tile token][k] (expert << 16 | rank), -1 if not kept
+};
+
+__device__ __forceinline__ LayoutLds layout_lds(int K) {
     extern __shared__ uint64_t lds[];
+    LayoutLds v;
+    v.masks = lds;
+    v.wpre = reinterpret_cast<int32_t *>(lds + kTileWaves * K);
+    v.excl = v.wpre + kTileWaves * K;
+    v.agg = v.excl + K;
+    v.scan = v.wpre;
+    v.slots = v.agg + K;
+    return v;
+}
+
+// The token's k slots (-1 past k or past the last token). The row index is
+// clamped and every load issued, so that the wait for them is exact and the
+// loads the caller issues next stay in flight.
+template <int KMAX>
+__device__ __forceinline__ void load_slots(const LayoutArgs &a, int t, int (&raw)[KMAX]) {
+    const int tc = max(min(t, a.T - 1), 0);
+    const int32_t *row = a.topk + (size_t)tc * a.k;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) raw[j] = row[min(j, a.k - 1)];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j)
+        if (t >= a.T || j >= a.k) raw[j] = -1;
+}
+
+__device__ __forceinline__ uint32_t load_epoch(const LayoutArgs &a) {
+    return __hip_atomic_load(&a.counters[kEpoch], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The layout of tile `tile` (its 256 tokens are t0 + thread), given the
+// thread's slots `raw` and the call's epoch. A single tile may run as `nrep`
+// replicas that split the outputs (replica = this copy); several tiles chain
+// through a decoupled look-back. In a fused launch the tile raises the flags
+// the dispatch waves wait on.
+template <int KMAX>
+__device__ __forceinline__ void layout_block(const LayoutArgs &a, int tile, int replica, int nrep, int mode,
+                                             const int (&raw)[KMAX], uint32_t epoch) {
     const int K = a.E + a.R;                   // keys: experts, then ranks
-    uint64_t *masks = lds;                     // [4 waves][K] token bitmasks per wave
-    int32_t *wpre = reinterpret_cast<int32_t *>(masks + kTileWaves * K);  // [4][K] tokens in earlier waves
-    int32_t *excl = wpre + kTileWaves * K;     // [K] tokens in earlier tiles
-    int32_t *agg = excl + K;                   // [K] tokens in this tile
-    int32_t *scan = wpre;                      // last step only: [E+1] prefix of expert rows
-    __shared__ int s_tile, s_part[kTileWaves + 1];
+    const LayoutLds L = layout_lds(K);
+    uint64_t *masks = L.masks;
+    int32_t *wpre = L.wpre, *excl = L.excl, *agg = L.agg, *scan = L.scan;
+    __shared__ int s_part[kTileWaves + 1];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const bool single = a.num_tiles == 1;
+    const bool fused = mode == kLayoutFlags;
+    const bool inblock = mode == kLayoutInBlock;  // (single tile only)
 
-    // A tile only waits on lower-numbered tiles. Small grids are co-resident,
-    // so the block index is the tile; larger grids number tiles in the order
-    // they start (a ticket), so every predecessor is already running.
-    // One tile: the grid is a few replicas of it, each writing a slice of the
-    // outputs (no cross-block traffic). Several tiles: block = tile.
-    const int replica = single ? (int)blockIdx.x : 0;
-    const int nrep = single ? (int)gridDim.x : 1;
-    int tile = single ? 0 : (int)blockIdx.x;
-    if (a.use_ticket) {
-        if (tid == 0) s_tile = (int)atomicAdd(&a.counters[kTicket], 1u);
-        __syncthreads();
-        tile = s_tile;
-    }
-    if (tile >= a.num_tiles) {  // workspace not re-armed (an earlier call did not finish)
-        if (tid == 0) atomicOr(&a.counters[kStatus], kStTimeout);
-        return;
-    }
     const int t0 = tile * kTileTokens;
     const int t = t0 + tid;
     const int ntile = max(min(kTileTokens, a.T - t0), 0);  // tokens in this tile
@@ -180,17 +217,9 @@ __global__ __launch_bounds__(kTileTokens) void k_layout(LayoutArgs a) {
         publish = first_hi > first_lo && first_hi * a.tpr - 1 >= t0 + kTileTokens;
     }
 
-    // the token's slots are requested first; their latency covers the setup
-    int raw[KMAX];
-    {
-        const int32_t *row = a.topk + (size_t)t * a.k;
-#pragma unroll
-        for (int j = 0; j < KMAX; ++j) raw[j] = (t < a.T && j < a.k) ? row[j] : -1;
-    }
-    uint32_t epoch = 0;
-    if (!single) epoch = __hip_atomic_load(&a.counters[kEpoch], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    for (int i = tid; i < kTileWaves * K; i += kTileTokens) masks[i] = 0;
-    __syncthreads();
+    // each wave clears its own masks (LDS operations of a wave are ordered):
+    // no barrier before the atomics
+    for (int i = lane; i < K; i += 64) masks[wave * K + i] = 0;
 
     // 1. validate the token's slots; expert bits go into the wave's masks
     //    (LDS atomics), the per-rank bits are wave ballots (no atomics: every
@@ -216,7 +245,7 @@ __global__ __launch_bounds__(kTileTokens) void k_layout(LayoutArgs a) {
         }
         ev[j] = v;
         atomicOr(reinterpret_cast<unsigned long long *>(&masks[wave * K + v]), (unsigned long long)bit);
-        rmask |= 1ull << (v / a.epr);
+        rmask |= 1ull << rank_of(v, a.epr, a.epr_shift);
     }
     {
         uint64_t mine = 0;
@@ -229,25 +258,6 @@ __global__ __launch_bounds__(kTileTokens) void k_layout(LayoutArgs a) {
     // tokens whose per-token outputs this block writes (all of them unless replicated)
     const int tok_chunk = (ntile + nrep - 1) / nrep;
     const bool my_token = t < a.T && tid >= replica * tok_chunk && tid < (replica + 1) * tok_chunk;
-    if (my_token) {
-        // is_token_in_rank row: R bytes, written with the widest aligned stores
-        uint8_t *out = a.itr + (size_t)t * a.R;
-        if ((a.R & 15) == 0) {
-            for (int d = 0; d < a.R; d += 16) {
-                const u32x4 v4 = {rank_bytes4(rmask, d), rank_bytes4(rmask, d + 4), rank_bytes4(rmask, d + 8),
-                                  rank_bytes4(rmask, d + 12)};
-                *reinterpret_cast<u32x4 *>(out + d) = v4;
-            }
-        } else if ((a.R & 7) == 0) {
-            for (int d = 0; d < a.R; d += 8)
-                *reinterpret_cast<uint64_t *>(out + d) =
-                    (uint64_t)rank_bytes4(rmask, d) | ((uint64_t)rank_bytes4(rmask, d + 4) << 32);
-        } else if ((a.R & 3) == 0) {
-            for (int d = 0; d < a.R; d += 4) *reinterpret_cast<uint32_t *>(out + d) = rank_bytes4(rmask, d);
-        } else {
-            for (int d = 0; d < a.R; ++d) out[d] = (uint8_t)((rmask >> d) & 1);
-        }
-    }
     if (st && replica == 0) atomicOr(&a.counters[kStatus], st);
     __syncthreads();
 
@@ -273,10 +283,12 @@ __global__ __launch_bounds__(kTileTokens) void k_layout(LayoutArgs a) {
     //    prefix; a predecessor that has not published yet ends the window and
     //    is read again. Then this tile's share of the per-source outputs:
     //    prefixes at the source-rank boundaries it owns (boundary s = token
-    //    s*T/R): src_expert_off directly, and a copy for later tiles.
+    //    s*T/R): src_expert_off directly, and a copy for later tiles. The
+    //    tile's stores come after its look-back loads (stores and loads share
+    //    one in-order completion counter).
     for (int key = tid; key < K; key += kTileTokens) {
         int sum = 0;
-        if (tile > 0) {
+        if (!single && tile > 0) {
             int hi = tile - 1;
             uint32_t spins = 0;
             while (hi >= 0) {
@@ -338,18 +350,19 @@ __global__ __launch_bounds__(kTileTokens) void k_layout(LayoutArgs a) {
             }
         }
     }
+    if (publish) __threadfence();  // every wave's prefix stores complete before the flag
     __syncthreads();
     if (!single && tid == 0) {
         if (publish) {
             // the start prefixes of the source that ends in a later tile are
             // visible from here on
-            __threadfence();
             __hip_atomic_store(a.bp_ready + tile, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-        if (last_tile) {
-            // The last tile's look-back has (transitively) seen every tile's
-            // published count, and a tile publishes only after reading the
-            // epoch: the workspace can be re-armed for the next call now.
+        // Re-arm the workspace for the next call once every tile has read
+        // the epoch: the last tile's look-back has (transitively) seen every
+        // tile's count, and a tile publishes only after reading the epoch.
+        // (Fused grids re-arm when their last block ends.)
+        if (!fused && last_tile) {
             uint32_t ne = (epoch + 1u) & ((1u << 30) - 1u);
             if (ne == 0) ne = 1;
             __hip_atomic_store(&a.counters[kTicket], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -358,25 +371,61 @@ __global__ __launch_bounds__(kTileTokens) void k_layout(LayoutArgs a) {
     }
 
     // 4. stable rank of each kept slot: tokens before it in earlier tiles,
-    //    earlier waves of this tile, and earlier lanes of its wave
-    if (my_token) {
+    //    earlier waves of this tile, and earlier lanes of its wave (in-block:
+    //    every token's, kept in LDS for the block's dispatch waves)
+    int r[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) r[j] = -1;
+    if (my_token || (inblock && t < a.T)) {
         const uint64_t below = bit - 1;
-        int r[KMAX];
 #pragma unroll
         for (int j = 0; j < KMAX; ++j) {
             const int e = ev[j];
             r[j] = e >= 0 ? excl[e] + wpre[wave * K + e] + __popcll(masks[wave * K + e] & below) : -1;
         }
-        int32_t *rie = a.rank_in_expert + (size_t)t * a.k;
-        if ((a.k & 3) == 0) {
-#pragma unroll
-            for (int j = 0; j < KMAX; j += 4)
-                if (j < a.k) *reinterpret_cast<int4 *>(rie + j) = make_int4(r[j], r[j + 1], r[j + 2], r[j + 3]);
-        } else {
+        if (inblock) {
 #pragma unroll
             for (int j = 0; j < KMAX; ++j)
-                if (j < a.k) rie[j] = r[j];
+                if (j < a.k) L.slots[tid * a.k + j] = ev[j] >= 0 ? (ev[j] << 16) | r[j] : -1;
         }
+        if (my_token) {
+            // is_token_in_rank row: R bytes, written with the widest aligned stores
+            uint8_t *out = a.itr + (size_t)t * a.R;
+            if ((a.R & 15) == 0) {
+                for (int d = 0; d < a.R; d += 16) {
+                    const u32x4 v4 = {rank_bytes4(rmask, d), rank_bytes4(rmask, d + 4), rank_bytes4(rmask, d + 8),
+                                      rank_bytes4(rmask, d + 12)};
+                    *reinterpret_cast<u32x4 *>(out + d) = v4;
+                }
+            } else if ((a.R & 7) == 0) {
+                for (int d = 0; d < a.R; d += 8)
+                    *reinterpret_cast<uint64_t *>(out + d) =
+                        (uint64_t)rank_bytes4(rmask, d) | ((uint64_t)rank_bytes4(rmask, d + 4) << 32);
+            } else if ((a.R & 3) == 0) {
+                for (int d = 0; d < a.R; d += 4) *reinterpret_cast<uint32_t *>(out + d) = rank_bytes4(rmask, d);
+            } else {
+                for (int d = 0; d < a.R; ++d) out[d] = (uint8_t)((rmask >> d) & 1);
+            }
+            int32_t *rie = a.rank_in_expert + (size_t)t * a.k;
+            if ((a.k & 3) == 0) {
+#pragma unroll
+                for (int j = 0; j < KMAX; j += 4)
+                    if (j < a.k) *reinterpret_cast<int4 *>(rie + j) = make_int4(r[j], r[j + 1], r[j + 2], r[j + 3]);
+            } else {
+#pragma unroll
+                for (int j = 0; j < KMAX; ++j)
+                    if (j < a.k) rie[j] = r[j];
+            }
+        }
+    }
+
+    if (fused) {
+        // this block's ranks are readable by the dispatch waves from here on
+        __threadfence();
+        __syncthreads();
+        if (tid == 0)
+            __hip_atomic_store(a.rank_ready + (single ? replica : tile), epoch, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
     }
 
     // 5. per-source counts for the source ranks that end in this tile
@@ -384,7 +433,9 @@ __global__ __launch_bounds__(kTileTokens) void k_layout(LayoutArgs a) {
     //    earlier tile is read back once that tile has published its prefixes
     if (!single && last_hi > last_lo) {
         const bool remote = last_lo * a.tpr < t0;  // only the first such source can start earlier
+        int32_t *remote_lo = wpre;                 // [K] its start prefixes (wpre is free after step 4)
         if (remote) {
+            __syncthreads();  // every wave is past step 4
             if (tid == 0) {
                 const int owner = (last_lo * a.tpr) / kTileTokens;
                 uint32_t spins = 0;
@@ -398,15 +449,16 @@ __global__ __launch_bounds__(kTileTokens) void k_layout(LayoutArgs a) {
                 __threadfence();
             }
             __syncthreads();
+            for (int key = tid; key < K; key += kTileTokens)
+                remote_lo[key] = __hip_atomic_load(a.bp + (size_t)last_lo * K + key, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
         }
         for (int key = tid; key < K; key += kTileTokens) {
             const KeyView kv = key_view(masks, K, key);
             const int ex = excl[key];
             for (int s = last_lo; s < last_hi; ++s) {
                 const int hi = ex + count_before(kv, (s + 1) * a.tpr - t0, ntile);
-                const int lo = s * a.tpr >= t0 ? ex + count_before(kv, s * a.tpr - t0, ntile)
-                                               : __hip_atomic_load(a.bp + (size_t)s * K + key, __ATOMIC_RELAXED,
-                                                                   __HIP_MEMORY_SCOPE_AGENT);
+                const int lo = s * a.tpr >= t0 ? ex + count_before(kv, s * a.tpr - t0, ntile) : remote_lo[key];
                 if (key < a.E)
                     a.cnt_se[(size_t)s * a.E + key] = hi - lo;
                 else
@@ -416,8 +468,9 @@ __global__ __launch_bounds__(kTileTokens) void k_layout(LayoutArgs a) {
     }
 
     // 6. the last tile holds every key's total: rows per expert, expert
-    //    offsets inside each rank (block scan), rows per rank
-    if (last_tile && replica == 0) {
+    //    offsets inside each rank (block scan), rows per rank. Replica 0
+    //    writes them; in-block copies keep the scan to place their own slots.
+    if (last_tile && (replica == 0 || inblock)) {
         __syncthreads();  // wpre is reused as the scan array below
         const int chunk = (a.E + kTileTokens - 1) / kTileTokens;
         const int lo = min(tid * chunk, a.E), hi = min(lo + chunk, a.E);
@@ -431,34 +484,114 @@ __global__ __launch_bounds__(kTileTokens) void k_layout(LayoutArgs a) {
         }
         if (tid == 0) scan[a.E] = total;
         __syncthreads();
-        for (int e = tid; e < a.E; e += kTileTokens) {
-            a.recv_cnt[e] = excl[e] + agg[e];
-            a.expert_off[e] = scan[e] - scan[(e / a.epr) * a.epr];
-        }
-        for (int d = tid; d < a.R; d += kTileTokens) {
-            const int rows = scan[(d + 1) * a.epr] - scan[d * a.epr];
-            a.rank_rows[d] = rows;
-            if ((int64_t)rows > a.cap_rows) atomicOr(&a.counters[kStatus], kStCap);
+        if (replica == 0) {
+            for (int e = tid; e < a.E; e += kTileTokens) {
+                a.recv_cnt[e] = excl[e] + agg[e];
+                a.expert_off[e] = scan[e] - scan[rank_of(e, a.epr, a.epr_shift) * a.epr];
+            }
+            for (int d = tid; d < a.R; d += kTileTokens) {
+                const int rows = scan[(d + 1) * a.epr] - scan[d * a.epr];
+                a.rank_rows[d] = rows;
+                if ((int64_t)rows > a.cap_rows) atomicOr(&a.counters[kStatus], kStCap);
+            }
+            if (fused) {
+                // expert offsets are readable by the dispatch waves from here on
+                __threadfence();
+                __syncthreads();
+                if (tid == 0)
+                    __hip_atomic_store(&a.counters[kTotalsReady], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
         }
     }
+}
+
+// Which tile (and replica) a block of a layout grid computes; -1: none.
+// Grids larger than the co-resident limit number tiles by start order (a
+// ticket), so that every predecessor is already running.
+__device__ __forceinline__ int layout_tile_of_block(const LayoutArgs &a, int b, int nblocks, int *replica, int *nrep) {
+    __shared__ int s_tile;
+    *replica = 0;
+    *nrep = 1;
+    if (a.num_tiles == 1) {
+        *replica = b;
+        *nrep = nblocks;
+        return 0;
+    }
+    if (!a.use_ticket) return b;
+    if (threadIdx.x == 0) s_tile = (int)atomicAdd(&a.counters[kTicket], 1u);
+    __syncthreads();
+    const int tile = s_tile;
+    if (tile >= a.num_tiles) {  // workspace not re-armed (an earlier call did not finish)
+        if (threadIdx.x == 0) atomicOr(&a.counters[kStatus], kStTimeout);
+        return -1;
+    }
+    return tile;
+}
+
+template <int KMAX>
+__global__ __launch_bounds__(kTileTokens) void k_layout(LayoutArgs a) {
+    int replica, nrep;
+    const int tile = layout_tile_of_block(a, (int)blockIdx.x, (int)gridDim.x, &replica, &nrep);
+    if (tile < 0) return;  // uniform over the block
+    int raw[KMAX];
+    load_slots<KMAX>(a, tile * kTileTokens + (int)threadIdx.x, raw);
+    const uint32_t epoch = load_epoch(a);  // (left in flight past the slots)
+    layout_block<KMAX>(a, tile, replica, nrep, kLayoutAlone, raw, epoch);
 }
 
 // ---------------------------------------------------------------------------
 // dispatch
 // ---------------------------------------------------------------------------
 
-// Slot j's receive row lives in lane j (lanes >= k hold -1).
-template <bool FWD>
+// What a dispatch wave of a fused launch waits for before reading the layout.
+struct LayoutWait {
+    const uint32_t *rank_ready;    // per layout block: epoch once its ranks are written
+    const uint32_t *totals_ready;  // epoch once the expert offsets are written
+    uint32_t *status;
+    uint32_t epoch, spin_limit;
+    int tokens_per_block;          // tokens whose ranks one layout block writes
+};
+
+// One thread of the block polls the flags of the layout blocks that wrote
+// the ranks of tokens [t_first, t_last] and the totals; the block waits at a
+// barrier (few pollers: the flags are single words every block reads).
+__device__ __forceinline__ void wait_for_layout(const LayoutWait &w, int t_first, int t_last) {
+    if (threadIdx.x == 0) {
+        const int lo = t_first / w.tokens_per_block, hi = t_last / w.tokens_per_block;
+        uint32_t spins = 0;
+        for (;;) {
+            bool ready = __hip_atomic_load(w.totals_ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == w.epoch;
+            for (int b = lo; b <= hi && ready; ++b)
+                ready = __hip_atomic_load(w.rank_ready + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == w.epoch;
+            if (ready) break;
+            if (++spins > w.spin_limit) {
+                atomicOr(w.status, kStTimeout);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(8);
+        }
+    }
+    __syncthreads();
+}
+
+// Slot j's receive row lives in lane j (lanes >= k hold -1). In a fused
+// launch the layout was written by other blocks of the same grid, so it is
+// read with coherent (agent-scope) loads.
+template <bool FWD, bool FUSED>
 __device__ __forceinline__ int slot_row(const DispatchArgs &a, int t, int lane, int part) {
     int p = -1;
     if (lane < a.k) {
         const size_t i = (size_t)t * a.k + lane;
         if (FWD) {
             const int e = a.topk[i];
-            const int r = a.rank_in_expert[i];
+            const int r = FUSED ? __hip_atomic_load(a.rank_in_expert + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                : a.rank_in_expert[i];
             if (r >= 0 && e >= 0 && e < a.E) {
-                const int64_t local = (int64_t)a.expert_off[e] + r;
-                if (local < a.cap_rows) p = (int)((int64_t)(e / a.epr) * a.cap_rows + local);
+                const int eo = FUSED ? __hip_atomic_load(a.expert_off + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                     : a.expert_off[e];
+                const int64_t local = (int64_t)eo + r;
+                if (local >= 0 && local < a.cap_rows)
+                    p = (int)((int64_t)rank_of(e, a.epr, a.epr_shift) * a.cap_rows + local);
             }
             if (part == 0) {
                 a.pos[i] = p;
@@ -478,27 +611,22 @@ __device__ __forceinline__ int slot_row(const DispatchArgs &a, int t, int lane, 
     return p;
 }
 
-template <bool FP8, bool FWD>
-__global__ __launch_bounds__(kWavesPerBlock * 64) void k_dispatch(DispatchArgs a) {
+// The bf16 source of this wave's passes, all loads issued at once (read
+// once: non-temporal). FP8: 16 channels per lane per pass; BF16: two 8-channel
+// vectors per lane, 512 channels apart.
+template <bool FP8>
+__device__ __forceinline__ void load_rows(const DispatchArgs &a, int t, int part, bool active,
+                                          u32x4 (&v)[2 * kMaxPassPerWave]) {
     const int lane = threadIdx.x & 63;
-    const int gw = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-    const int t = gw / a.waves_per_token;
-    const int part = gw - t * a.waves_per_token;
-    if (t >= a.T) return;  // whole wave
-
     const int pass0 = part * a.passes_per_wave;
     const int np = min(a.passes_per_wave, a.npass - pass0);
     const int H = a.H;
     const uint16_t *xrow = a.x + (size_t)t * H;
-
-    // issue every load of this wave's passes first (read-once: non-temporal);
-    // the slot rows are looked up while they are in flight
-    u32x4 v[2 * kMaxPassPerWave];
 #pragma unroll
     for (int i = 0; i < kMaxPassPerWave; ++i) {
         v[2 * i] = 0;
         v[2 * i + 1] = 0;
-        if (i < np) {
+        if (active && i < np) {
             const int ps = pass0 + i;
             if (FP8) {
                 const int c = ps * 1024 + lane * 16;  // 16 channels per lane
@@ -515,11 +643,19 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void k_dispatch(DispatchArgs a
             }
         }
     }
+}
 
-    const int p = slot_row<FWD>(a, t, lane, part);
-
-    // receive rows are written with ordinary (cache-allocating) stores: on
-    // gfx950 they sustain a higher write rate than non-temporal ones here
+// Quantize (FP8) or copy (BF16) the wave's passes into the receive rows of
+// its token's kept slots (slot j's row in lane j of p). Rows are written with
+// ordinary (cache-allocating) stores: on gfx950 they sustain a higher write
+// rate than non-temporal ones here.
+template <bool FP8>
+__device__ __forceinline__ void store_rows(const DispatchArgs &a, int part, int p,
+                                           const u32x4 (&v)[2 * kMaxPassPerWave]) {
+    const int lane = threadIdx.x & 63;
+    const int pass0 = part * a.passes_per_wave;
+    const int np = min(a.passes_per_wave, a.npass - pass0);
+    const int H = a.H;
 #pragma unroll
     for (int i = 0; i < kMaxPassPerWave; ++i) {
         if (i >= np) break;
@@ -586,6 +722,140 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void k_dispatch(DispatchArgs a
             }
         }
     }
+}
+
+template <bool FP8, bool FWD>
+__global__ __launch_bounds__(kWavesPerBlock * 64) void k_dispatch(DispatchArgs a) {
+    const int gw = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+    const int t = gw / a.waves_per_token;
+    const int part = gw - t * a.waves_per_token;
+    if (t >= a.T) return;  // whole wave
+    u32x4 v[2 * kMaxPassPerWave];
+    load_rows<FP8>(a, t, part, true, v);  // in flight while the slot rows are looked up
+    const int p = slot_row<FWD, false>(a, t, threadIdx.x & 63, part);
+    store_rows<FP8>(a, part, p, v);
+}
+
+// Slot j's receive row (lane j) from the layout this block holds in LDS
+// (in-block mode: single tile, so the token's index is its tile position).
+__device__ __forceinline__ int slot_row_lds(const DispatchArgs &a, const LayoutLds &L, int t, int lane, int part,
+                                            float wslot) {
+    int p = -1;
+    if (lane < a.k) {
+        const int sv = L.slots[t * a.k + lane];
+        if (sv >= 0) {
+            const int e = sv >> 16, r = sv & 0xFFFF;
+            const int d = rank_of(e, a.epr, a.epr_shift);
+            const int64_t local = (int64_t)(L.scan[e] - L.scan[d * a.epr]) + r;
+            if (local < a.cap_rows) p = (int)((int64_t)d * a.cap_rows + local);
+        }
+        if (part == 0) {
+            const size_t i = (size_t)t * a.k + lane;
+            a.pos[i] = p;
+            if (p >= 0) {
+                a.src_idx[p] = t;
+                if (a.recv_w) a.recv_w[p] = wslot;
+            }
+        }
+    }
+    return p;
+}
+
+// Layout and forward dispatch of one tile (T <= 256) in one grid with no
+// cross-block waits: every block loads its rows, builds the whole layout in
+// LDS (writing its share of the layout outputs, like a replica), and places
+// its rows from there.
+template <int KMAX, bool FP8>
+__global__ __launch_bounds__(kTileTokens) void k_dispatch_inblock(LayoutArgs la, DispatchArgs da) {
+    const int gw = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+    const int t = gw / da.waves_per_token;
+    const int part = gw - t * da.waves_per_token;
+    const bool active = t < da.T;  // whole wave
+    const int lane = threadIdx.x & 63;
+    // loads before any store (stores share the in-order counter): the
+    // slots the layout waits on first, the slot weight, then the rows
+    int raw[KMAX];
+    load_slots<KMAX>(la, (int)threadIdx.x, raw);
+    const float wslot = (active && part == 0 && lane < da.k && da.recv_w) ? da.w[(size_t)t * da.k + lane] : 0.0f;
+    u32x4 v[2 * kMaxPassPerWave];
+    load_rows<FP8>(da, t, part, active, v);
+    layout_block<KMAX>(la, 0, (int)blockIdx.x, (int)gridDim.x, kLayoutInBlock, raw, 0u);  // ends at a barrier
+    if (!active) return;
+    const int p = slot_row_lds(da, layout_lds(la.E + la.R), t, lane, part, wslot);
+    store_rows<FP8>(da, part, p, v);
+}
+
+// The dispatch side of a fused grid with flags: the block's NW waves load
+// (and, for FP8, later quantize) their rows before the layout is known, wait
+// for the layout blocks of their tokens and for the totals, then write the
+// rows. `db` is the block's index among the dispatch blocks.
+template <bool FP8, int NW>
+__device__ __forceinline__ void fused_dispatch_block(const DispatchArgs &da, const LayoutWait &lw, int db) {
+    const int gw = db * NW + (int)(threadIdx.x >> 6);
+    const int t = gw / da.waves_per_token;
+    const int part = gw - t * da.waves_per_token;
+    const bool active = t < da.T;  // whole wave
+    u32x4 v[2 * kMaxPassPerWave];
+    load_rows<FP8>(da, t, part, active, v);  // loaded before the layout is known
+    // every wave of the block reaches the barrier inside
+    const int gw0 = db * NW;
+    const int t_first = min(gw0 / da.waves_per_token, da.T - 1);
+    const int t_last = min((gw0 + NW - 1) / da.waves_per_token, da.T - 1);
+    wait_for_layout(lw, t_first, t_last);
+    if (active) {
+        const int p = slot_row<true, true>(da, t, threadIdx.x & 63, part);
+        store_rows<FP8>(da, part, p, v);
+    }
+}
+
+__device__ __forceinline__ LayoutWait make_wait(const LayoutArgs &la, uint32_t epoch, int tokens_per_block) {
+    LayoutWait lw;
+    lw.rank_ready = la.rank_ready;
+    lw.totals_ready = la.counters + kTotalsReady;
+    lw.status = la.counters + kStatus;
+    lw.epoch = epoch;
+    lw.spin_limit = la.spin_limit;
+    lw.tokens_per_block = max(tokens_per_block, 1);
+    return lw;
+}
+
+// End of a fused grid: the last block to finish re-arms the workspace
+// (every block has read the epoch by then).
+__device__ __forceinline__ void fused_rearm(const LayoutArgs &la) {
+    __syncthreads();
+    if (threadIdx.x == 0 && atomicAdd(&la.counters[kDone], 1u) == gridDim.x - 1) {
+        const uint32_t epoch = __hip_atomic_load(&la.counters[kEpoch], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        uint32_t ne = (epoch + 1u) & ((1u << 30) - 1u);
+        if (ne == 0) ne = 1;
+        __hip_atomic_store(&la.counters[kTicket], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&la.counters[kDone], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&la.counters[kEpoch], ne, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// Layout and forward dispatch in one grid: blocks [0, lgrid) compute the
+// layout (the tiles, or the replicas of one tile), the rest are dispatch
+// waves that load and quantize their rows first and wait for the layout only
+// to place them. Layout blocks have the lowest indices, so they are running
+// before any dispatch block waits.
+template <int KMAX, bool FP8>
+__global__ __launch_bounds__(kTileTokens) void k_layout_dispatch(LayoutArgs la, DispatchArgs da, int lgrid) {
+    const int b = (int)blockIdx.x;
+    if (b < lgrid) {
+        int replica, nrep;
+        const int tile = layout_tile_of_block(la, b, lgrid, &replica, &nrep);
+        if (tile >= 0) {
+            int raw[KMAX];
+            load_slots<KMAX>(la, tile * kTileTokens + (int)threadIdx.x, raw);
+            const uint32_t epoch = load_epoch(la);
+            layout_block<KMAX>(la, tile, replica, nrep, kLayoutFlags, raw, epoch);
+        }
+    } else {
+        const uint32_t epoch = load_epoch(la);
+        const int tpb = la.num_tiles > 1 ? kTileTokens : (la.T + lgrid - 1) / lgrid;
+        fused_dispatch_block<FP8, kWavesPerBlock>(da, make_wait(la, epoch, tpb), b - lgrid);
+    }
+    fused_rearm(la);
 }
 
 // ---------------------------------------------------------------------------
@@ -723,6 +993,44 @@ hipError_t launch_layout(const LayoutArgs &a, hipStream_t s) {
         hipLaunchKernelGGL(k_layout<8>, dim3(grid), dim3(kTileTokens), lds, s, a);
     else
         hipLaunchKernelGGL(k_layout<kMaxTopk>, dim3(grid), dim3(kTileTokens), lds, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_layout_dispatch(const LayoutArgs &la, const DispatchArgs &da, bool fp8, int num_waves,
+                                  hipStream_t s) {
+    const size_t lds = layout_lds_bytes(la.E + la.R);
+    const int lgrid = la.num_tiles > 1 ? la.num_tiles : max(1, min(la.R, kLayoutReplicas));
+    const int grid = lgrid + (num_waves + kWavesPerBlock - 1) / kWavesPerBlock;
+    const dim3 block(kTileTokens);
+    if (la.k <= 8) {
+        if (fp8)
+            hipLaunchKernelGGL((k_layout_dispatch<8, true>), dim3(grid), block, lds, s, la, da, lgrid);
+        else
+            hipLaunchKernelGGL((k_layout_dispatch<8, false>), dim3(grid), block, lds, s, la, da, lgrid);
+    } else {
+        if (fp8)
+            hipLaunchKernelGGL((k_layout_dispatch<kMaxTopk, true>), dim3(grid), block, lds, s, la, da, lgrid);
+        else
+            hipLaunchKernelGGL((k_layout_dispatch<kMaxTopk, false>), dim3(grid), block, lds, s, la, da, lgrid);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_dispatch_inblock(const LayoutArgs &la, const DispatchArgs &da, bool fp8, int num_waves,
+                                   hipStream_t s) {
+    const size_t lds = inblock_lds_bytes(la.E + la.R, la.k);
+    const dim3 grid((num_waves + kWavesPerBlock - 1) / kWavesPerBlock), block(kTileTokens);
+    if (la.k <= 8) {
+        if (fp8)
+            hipLaunchKernelGGL((k_dispatch_inblock<8, true>), grid, block, lds, s, la, da);
+        else
+            hipLaunchKernelGGL((k_dispatch_inblock<8, false>), grid, block, lds, s, la, da);
+    } else {
+        if (fp8)
+            hipLaunchKernelGGL((k_dispatch_inblock<kMaxTopk, true>), grid, block, lds, s, la, da);
+        else
+            hipLaunchKernelGGL((k_dispatch_inblock<kMaxTopk, false>), grid, block, lds, s, la, da);
+    }
     return hipGetLastError();
 }
 

@@ -71,6 +71,9 @@ SIGNATURES = {
     "ep_dispatch": (ctypes.c_int, [c_void_p, c_void_p, c_void_p, c_void_p, ctypes.POINTER(EpLayout),
                                    ctypes.c_int, c_void_p, c_void_p, c_void_p,
                                    ctypes.POINTER(EpHandle), c_void_p]),
+    "ep_dispatch_with_layout": (ctypes.c_int, [c_void_p, c_void_p, c_void_p, c_void_p, ctypes.POINTER(EpLayout),
+                                               ctypes.c_int, c_void_p, c_void_p, c_void_p,
+                                               ctypes.POINTER(EpHandle), c_void_p]),
     "ep_combine": (ctypes.c_int, [c_void_p, c_void_p, ctypes.POINTER(EpHandle), c_void_p, c_void_p,
                                   c_void_p]),
     "ep_combine_f32": (ctypes.c_int, [c_void_p, c_void_p, ctypes.POINTER(EpHandle), c_void_p,
@@ -151,6 +154,14 @@ def ep_dispatch(ctx: int, x: int, topk_idx: int, topk_weights: Optional[int], la
                 handle: EpHandle, stream: int) -> None:
     _check(load().ep_dispatch(ctx, x, topk_idx, topk_weights, ctypes.byref(layout), int(use_fp8),
                               recv_x, recv_scales, recv_w, ctypes.byref(handle), stream), "ep_dispatch")
+
+
+def ep_dispatch_with_layout(ctx: int, x: int, topk_idx: int, topk_weights: Optional[int], layout: EpLayout,
+                            use_fp8: int, recv_x: int, recv_scales: Optional[int], recv_w: Optional[int],
+                            handle: EpHandle, stream: int) -> None:
+    _check(load().ep_dispatch_with_layout(ctx, x, topk_idx, topk_weights, ctypes.byref(layout), int(use_fp8),
+                                          recv_x, recv_scales, recv_w, ctypes.byref(handle), stream),
+           "ep_dispatch_with_layout")
 
 
 def ep_combine(ctx: int, expert_out: int, handle: EpHandle, weights: Optional[int],
@@ -308,6 +319,26 @@ class Buffer:
                     int(bool(use_fp8)), recv_x.data_ptr(), _ptr(recv_scales), _ptr(recv_w), ch, _stream())
         handle.num_tokens, handle.num_topk = ch.num_tokens, ch.num_topk
         return recv_x, recv_scales, recv_w, handle
+
+    def dispatch_with_layout(self, x, topk_idx, topk_weights, use_fp8: bool, layout: Optional[Layout] = None,
+                             out=None):
+        """Layout and dispatch in one launch. Returns (layout, recv_x,
+        recv_scales, recv_w, handle)."""
+        t = self.torch
+        layout = layout or self.new_layout()
+        if out is None:
+            recv_x = self._empty((self.num_rows, self.H), t.uint8 if use_fp8 else t.bfloat16)
+            recv_scales = self._empty((self.num_rows, self.H // 128), t.float32) if use_fp8 else None
+            recv_w = self._empty(self.num_rows, t.float32)
+            handle = self.new_handle()
+        else:
+            recv_x, recv_scales, recv_w, handle = out
+        ch = handle.c()
+        ep_dispatch_with_layout(self.ctx, x.data_ptr(), topk_idx.data_ptr(), _ptr(topk_weights), layout.c(),
+                                int(bool(use_fp8)), recv_x.data_ptr(), _ptr(recv_scales), _ptr(recv_w), ch,
+                                _stream())
+        handle.num_tokens, handle.num_topk = ch.num_tokens, ch.num_topk
+        return layout, recv_x, recv_scales, recv_w, handle
 
     def combine(self, expert_out, handle: Handle, weights=None, out=None):
         out = out if out is not None else self._empty((self.T, self.H), self.torch.bfloat16)

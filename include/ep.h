@@ -168,6 +168,19 @@ int ep_dispatch(ep_ctx *ctx, const uint16_t *x, const int32_t *topk_idx,
                 void *recv_x, float *recv_scales, float *recv_w, ep_handle *handle,
                 ep_stream_t stream);
 
+/* ep_get_dispatch_layout followed by ep_dispatch, in one launch: the same
+ * outputs (layout, handle, received rows, scales and weights), bit for bit.
+ * Up to 256 tokens every dispatch block computes the whole layout in its own
+ * LDS (no block waits on another); beyond that the layout blocks raise flags
+ * in the workspace and the dispatch waves, which have already loaded their
+ * rows of x, wait on them only to place the rows. Same arguments and
+ * requirements as the two calls it replaces; calls on one context are
+ * ordered by the stream (two streams sharing a context race). */
+int ep_dispatch_with_layout(ep_ctx *ctx, const uint16_t *x, const int32_t *topk_idx,
+                            const float *topk_weights, const ep_layout *layout, int use_fp8,
+                            void *recv_x, float *recv_scales, float *recv_w, ep_handle *handle,
+                            ep_stream_t stream);
+
 /* Combine (the guide's combine): weighted gather-reduce back to source-token
  * order. For each token t and channel i: acc = +0.0f; for j = 0..k-1 with
  * pos[t][j] >= 0: acc = fmaf(w[t][j], expert_out[pos[t][j]][i], acc) (w = 1

@@ -60,15 +60,19 @@ class GpuForward:
     w: torch.Tensor
 
 
-def gpu_forward(x_u16, topk_idx, topk_w, E, R, cap_rows, use_fp8, x_dev=None) -> GpuForward:
+def gpu_forward(x_u16, topk_idx, topk_w, E, R, cap_rows, use_fp8, x_dev=None, fused=False) -> GpuForward:
+    """Layout + dispatch through the C ABI: two calls, or the fused one."""
     T, k = topk_idx.shape
     H = x_u16.shape[1] if x_dev is None else x_dev.shape[1]
     buf = ep.Buffer(T, H, k, E, R, cap_rows)
     topk = dev(topk_idx.astype(np.int32))
     w = dev(topk_w.astype(np.float32))
     x = x_dev if x_dev is not None else dev_bf16(x_u16)
-    L = buf.get_dispatch_layout(topk)
-    recv_x, rs, rw, h = buf.dispatch(x, topk, w, L, use_fp8)
+    if fused:
+        L, recv_x, rs, rw, h = buf.dispatch_with_layout(x, topk, w, use_fp8)
+    else:
+        L = buf.get_dispatch_layout(topk)
+        recv_x, rs, rw, h = buf.dispatch(x, topk, w, L, use_fp8)
     st = buf.status()
     return GpuForward(buf, L, recv_x, rs, rw, h, st, topk, w)
 

@@ -25,11 +25,11 @@ def oracle_cap(topk, E, R):
     return int(oracle.layout(topk, E, R, 1 << 30).rank_rows.max())
 
 
-def full_check(x, topk, w, E, R, cap, use_fp8, expert_out_seed=5, check_combine=True):
+def full_check(x, topk, w, E, R, cap, use_fp8, expert_out_seed=5, check_combine=True, fused=False):
     """Layout + dispatch + combine (+ f32 sums) against the oracle, every element."""
     orc = oracle.default()
     L, pos, src, rx, rs, rw = orc.forward(x, topk, w, E, R, cap, use_fp8)
-    g = gpu_forward(x, topk, w, E, R, cap, use_fp8)
+    g = gpu_forward(x, topk, w, E, R, cap, use_fp8, fused=fused)
     assert g.status == L.status, (g.status, L.status)
     compare_layout(g, L)
     compare_handle(g, pos, src)
@@ -58,12 +58,13 @@ def full_check(x, topk, w, E, R, cap, use_fp8, expert_out_seed=5, check_combine=
 # the workloads, full element-wise parity
 # ---------------------------------------------------------------------------
 
+@pytest.mark.parametrize("fused", [False, True], ids=["two_calls", "fused"])
 @pytest.mark.parametrize("name", ["tiny", "decode_rank", "decode", "prefill", "skewed"])
-def test_forward_parity(name):
+def test_forward_parity(name, fused):
     cfg = CONFIGS[name]
     wl = make_workload(cfg, seed=0)
     cap = oracle_cap(wl.topk_idx, cfg.E, cfg.R)
-    full_check(wl.x, wl.topk_idx, wl.topk_w, cfg.E, cfg.R, cap, cfg.use_fp8)
+    full_check(wl.x, wl.topk_idx, wl.topk_w, cfg.E, cfg.R, cap, cfg.use_fp8, fused=fused)
 
 
 @pytest.mark.parametrize("seed", [1, 2, 3])
@@ -154,8 +155,9 @@ def sampled_checks(cfg, wl, g, pos, use_fp8, with_backward):
         assert compare_bf16(gxt, gx_o, "dispatch_backward (sampled)") == 1.0
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["two_calls", "fused"])
 @pytest.mark.parametrize("name", ["prefill", "large"])
-def test_full_size_sampled(name):
+def test_full_size_sampled(name, fused):
     cfg = CONFIGS[name]
     wl = make_workload(cfg, seed=0)
     orc = oracle.default()
@@ -163,7 +165,7 @@ def test_full_size_sampled(name):
     cap = int(L.rank_rows.max())
     L = orc.layout(wl.topk_idx, cfg.E, cfg.R, cap)
     pos, src = orc.positions(wl.topk_idx, L, cfg.E, cfg.R, cap)
-    g = gpu_forward(wl.x, wl.topk_idx, wl.topk_w, cfg.E, cfg.R, cap, cfg.use_fp8)
+    g = gpu_forward(wl.x, wl.topk_idx, wl.topk_w, cfg.E, cfg.R, cap, cfg.use_fp8, fused=fused)
     assert g.status == L.status == 0
     compare_layout(g, L)
     compare_handle(g, pos, src)
@@ -180,7 +182,7 @@ def rand_routing(rng, T, k, E):
     return np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32)
 
 
-def case(T, k, E, R, H, fp8, seed=0, mutate=None, cap=None, cap_delta=0):
+def case(T, k, E, R, H, fp8, seed=0, mutate=None, cap=None, cap_delta=0, fused=False):
     rng = np.random.default_rng(seed)
     topk = rand_routing(rng, T, k, E)
     if mutate is not None:
@@ -191,7 +193,7 @@ def case(T, k, E, R, H, fp8, seed=0, mutate=None, cap=None, cap_delta=0):
     x = to_bf16_bits(xf)
     if cap is None:
         cap = max(oracle_cap(topk, E, R) + cap_delta, 0)
-    return full_check(x, topk, w, E, R, cap, fp8)
+    return full_check(x, topk, w, E, R, cap, fp8, fused=fused)
 
 
 EDGE = {
@@ -211,12 +213,28 @@ EDGE = {
     "ticket_tiles": dict(T=270336, k=1, E=16, R=8, H=8, fp8=False),
     "multi_tile_4_waves": dict(T=4096, k=8, E=1024, R=64, H=256, fp8=True),
     "single_tile_16_waves_ragged": dict(T=1000, k=8, E=256, R=8, H=256, fp8=False),
+    # one tile whose layout does not fit beside the slots in a block's LDS
+    # (the fused call then uses separate layout blocks and flags)
+    "one_tile_E1024_R64": dict(T=192, k=8, E=1024, R=64, H=512, fp8=True),
+    # one tile, 32 slots per token: the largest in-block slot table
+    "one_tile_k32_E512": dict(T=96, k=32, E=512, R=32, H=384, fp8=True),
+    "one_full_tile": dict(T=256, k=8, E=256, R=8, H=7168, fp8=True),
+    # several tiles chained by look-back: a source rank per tile and a
+    # ragged last tile, wide rows, the most tiles whose source boundaries
+    # all fall on tile edges
+    "tiles_32": dict(T=8192, k=8, E=256, R=32, H=256, fp8=True),
+    "tiles_ragged": dict(T=5000, k=6, E=200, R=8, H=384, fp8=False),
+    "tiles_k16": dict(T=2048, k=16, E=128, R=16, H=256, fp8=True),
+    "tiles_33": dict(T=8448, k=8, E=256, R=32, H=256, fp8=True),
+    # experts per rank not a power of two (division instead of a shift)
+    "epr_not_pow2": dict(T=1536, k=8, E=192, R=8, H=256, fp8=True),
 }
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["two_calls", "fused"])
 @pytest.mark.parametrize("name", list(EDGE))
-def test_edge_shapes(name):
-    case(**EDGE[name])
+def test_edge_shapes(name, fused):
+    case(**EDGE[name], fused=fused)
 
 
 def test_all_slots_empty():
@@ -238,6 +256,18 @@ def test_all_to_one_expert():
         t[:, 1:] = -1
         return t
     case(T=2048, k=4, E=16, R=4, H=1024, fp8=True, mutate=m)
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["two_calls", "fused"])
+def test_capacity_and_bad_ids_fused(fused):
+    def m(t, r):
+        t = t.copy()
+        t[3, 1] = 99
+        t[5, 2] = t[5, 0]
+        return t
+    for T in (1024, 200):  # several tiles; one tile
+        g, (L, pos, *_ ) = case(T=T, k=8, E=64, R=8, H=512, fp8=True, cap_delta=-9, mutate=m, fused=fused)
+        assert L.status == ep.EP_ST_CAPACITY | ep.EP_ST_BAD_EXPERT | ep.EP_ST_DUP_EXPERT
 
 
 def test_bad_and_repeated_experts():
@@ -307,6 +337,32 @@ def test_fp8_all_bf16_patterns():
 # determinism, repeated calls on one context
 # ---------------------------------------------------------------------------
 
+def test_fused_and_separate_calls_interleaved():
+    """Fused and two-call forwards alternate on one context (both re-arm the
+    shared workspace): every call matches the oracle."""
+    cfg = replace(CONFIGS["prefill"], H=1024)
+    for seed in range(4):
+        wl = make_workload(cfg, seed=seed)
+        if seed == 0:
+            cap = oracle_cap(wl.topk_idx, cfg.E, cfg.R) + 64
+            buf = ep.Buffer(cfg.T, cfg.H, cfg.k, cfg.E, cfg.R, cap)
+        L_o, pos_o, src_o, rx_o, rs_o, rw_o = oracle.default().forward(wl.x, wl.topk_idx, wl.topk_w, cfg.E,
+                                                                       cfg.R, cap, True)
+        x, topk, w = dev_bf16(wl.x), dev(wl.topk_idx), dev(wl.topk_w)
+        for fused in (True, False):
+            if fused:
+                L, rx, rs, rw, h = buf.dispatch_with_layout(x, topk, w, True)
+            else:
+                L = buf.get_dispatch_layout(topk)
+                rx, rs, rw, h = buf.dispatch(x, topk, w, L, True)
+            assert buf.status() == 0
+            assert np.array_equal(host(h.pos), pos_o), (seed, fused)
+            assert np.array_equal(host(L.cnt_se), L_o.cnt_se) and np.array_equal(host(L.src_expert_off),
+                                                                                 L_o.src_expert_off)
+            rows = torch.from_numpy(used_rows(pos_o).astype(np.int64)).cuda()
+            assert np.array_equal(rx.index_select(0, rows).cpu().numpy(), rx_o[used_rows(pos_o)]), (seed, fused)
+
+
 def test_repeated_layouts_on_one_context():
     """The look-back states are re-armed by each call (epochs): ten calls with
     different routing on one context each match the oracle."""
@@ -357,12 +413,14 @@ def test_handle_from_other_config_rejected():
     b1.status()
 
 
-def test_graph_replay_matches_eager():
+@pytest.mark.parametrize("cfg_name", ["decode_rank", "decode"])  # one tile; four tiles
+@pytest.mark.parametrize("fused", [False, True], ids=["two_calls", "fused"])
+def test_graph_replay_matches_eager(fused, cfg_name):
     """The decode step (layout, FP8 dispatch, combine) captured in a HIP graph
     and replayed several times, with eager work and synchronizations between
     replays: every replay equals the eager result (the workspace re-arms
     itself on the device; the path records no memset)."""
-    cfg = CONFIGS["decode_rank"]
+    cfg = CONFIGS[cfg_name]
     wl = make_workload(cfg, seed=7)
     cap = oracle_cap(wl.topk_idx, cfg.E, cfg.R)
     buf = ep.Buffer(cfg.T, cfg.H, cfg.k, cfg.E, cfg.R, cap)
@@ -375,8 +433,11 @@ def test_graph_replay_matches_eager():
     y = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device="cuda")
 
     def step():
-        buf.get_dispatch_layout(topk, L)
-        buf.dispatch(x, topk, w, L, True, out=out)
+        if fused:
+            buf.dispatch_with_layout(x, topk, w, True, layout=L, out=out)
+        else:
+            buf.get_dispatch_layout(topk, L)
+            buf.dispatch(x, topk, w, L, True, out=out)
         buf.combine(eo, out[3], w, out=y)
 
     step()
