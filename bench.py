@@ -5,10 +5,14 @@
 
 One step = the whole forward hot path over one batch of the workload:
 dispatch layout -> FP8 dispatch (pack + quantize) -> combine (weighted
-gather-reduce to bf16), all inputs resident in HBM. `value` is dispatch +
-combine algorithmic bytes per second of step time (GB/s); the JSON line also
-carries the per-kernel breakdown, the roofline of the dominant kernel, the
-decode latency at 128 tokens, the backward pair, and the CPU oracle baseline.
+gather-reduce to bf16), all inputs resident in HBM. By default the layout
+and the dispatch are one launch (ep_dispatch_with_layout) and steps are
+captured in a HIP graph (up to 10 per graph) and replayed to run exactly K
+(--eager: plain launches; --separate: three calls). `value` is dispatch + combine algorithmic bytes per
+second of step time (GB/s); the JSON line also carries the eager step, the
+per-kernel breakdown (events around eager launches), the roofline of the
+dominant kernel, the decode latency at 128 tokens, the backward pair, and
+the CPU oracle baseline.
 """
 from __future__ import annotations
 
@@ -38,6 +42,8 @@ def parse():
     p.add_argument("--no-extras", action="store_true", help="skip decode/backward/copy extras")
     p.add_argument("--no-decode", action="store_true", help="skip the decode-latency extra")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--eager", action="store_true",
+                   help="time the step as eager launches instead of replays of a HIP graph holding one step")
     p.add_argument("--separate", action="store_true",
                    help="time the step as three calls (layout, dispatch, combine) instead of the fused "
                         "layout+dispatch launch followed by combine")
@@ -128,6 +134,39 @@ def timed(torch, ops, K, W):
     wall = time.perf_counter() - t0
     per_op = [sum(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(K)) / K for j in range(len(ops))]
     return wall / K * 1e3, per_op  # ms per step, ms per op
+
+
+def graph_step_timed(torch, ops, K, W):
+    """G consecutive steps captured in one HIP graph (G = the largest divisor
+    of K up to 10, as a forward pass captures its layers together); untimed
+    replays for the W warmup steps, then exactly K steps (K / G replays)
+    between synchronizations. Returns (ms per step by wall clock, ms per step
+    by events on the replay stream, G)."""
+    G = max(d for d in range(1, 11) if K % d == 0)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for op in ops:  # first calls (library load, allocations) outside the capture
+            op()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(G):
+            for op in ops:
+                op()
+    for _ in range((W + G - 1) // G):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(K // G):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall / K * 1e3, e0.elapsed_time(e1) / K, G
 
 
 def graph_timed(torch, ops, K, W, inner=20):
@@ -342,11 +381,19 @@ def main():
     torch.cuda.set_device(0)
     main_path = Path(cfg, args.seed, torch, ep, workloads)
     fused = not args.separate
+    main_ops = [main_path.fused_op, main_path.combine_op] if fused else \
+        [main_path.layout_op, main_path.dispatch_op, main_path.combine_op]
+    # eager launches with events around every op: the per-kernel durations
+    # (and the step itself with --eager)
+    eager_ms, per_op = timed(torch, main_ops, K, W)
     if fused:
-        ms, (ld_ms, com_ms) = timed(torch, [main_path.fused_op, main_path.combine_op], K, W)
+        ld_ms, com_ms = per_op
     else:
-        ms, (lay_ms, dis_ms, com_ms) = timed(torch, [main_path.layout_op, main_path.dispatch_op,
-                                                     main_path.combine_op], K, W)
+        lay_ms, dis_ms, com_ms = per_op
+    if args.eager:
+        ms, ms_events, per_graph = eager_ms, eager_ms, 0
+    else:
+        ms, ms_events, per_graph = graph_step_timed(torch, main_ops, K, W)
     st = main_path.buf.status()
     if st:
         raise SystemExit(f"bench: device status {st} on {cfg.name}")
@@ -372,13 +419,18 @@ def main():
         "config": {"workload": cfg.name, "tokens": cfg.T, "hidden": cfg.H, "experts": cfg.E,
                    "ranks_simulated": cfg.R, "topk": cfg.k, "routing": cfg.routing,
                    "fp8_dispatch": cfg.use_fp8, "cap_rows": main_path.cap, "kept_slots": N,
-                   "step": "fused layout+dispatch launch, then combine" if fused
-                   else "layout, dispatch, combine (three launches)"},
+                   "step": ("fused layout+dispatch launch, then combine" if fused
+                            else "layout, dispatch, combine (three launches)") +
+                           ("; eager launches" if args.eager else
+                            f"; HIP graph of {per_graph} steps, replayed {K // max(per_graph, 1)} times")},
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "kernel": "k_combine", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": c_bytes},
         "kernels": {},
+        "step_us_by_events": round(ms_events * 1e3, 2),
+        "eager_step": {"us_per_step": round(eager_ms * 1e3, 2),
+                       "GBps": round((d_bytes + c_bytes) / (eager_ms * 1e-3) / 1e9, 1)},
     }
     if fused:
         out["kernels"]["layout_dispatch"] = {"us": round(ld_ms * 1e3, 2), "bytes": d_bytes,
