@@ -135,6 +135,18 @@ __device__ __forceinline__ uint32_t rank_bytes4(uint64_t rmask, int d) {
 // of a single-tile fused grid (the block keeps the whole layout in its LDS).
 enum LayoutMode { kLayoutAlone = 0, kLayoutFlags = 1, kLayoutInBlock = 2 };
 
+// Publishing to other blocks of the same grid. Everything a dispatch wave
+// reads from the layout (ranks, expert offsets) is written with agent-scope
+// stores, which are coherent across XCDs by themselves; a block releases them
+// by having every thread wait until its stores are acknowledged (vmcnt also
+// counts stores) before the barrier that precedes the flag store. This is the
+// agent-scope release without the L2 write-back that plain stores would need
+// (that write-back competes with the grid's row traffic for several us).
+__device__ __forceinline__ void store_agent(int32_t *p, int v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_own_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // Expert e's rank: a shift when the experts per rank are a power of two.
 __device__ __forceinline__ int rank_of(int e, int epr, int shift) { return shift >= 0 ? e >> shift : e / epr; }
 
@@ -407,7 +419,11 @@ __device__ __forceinline__ void layout_block(const LayoutArgs &a, int tile, int 
                 for (int d = 0; d < a.R; ++d) out[d] = (uint8_t)((rmask >> d) & 1);
             }
             int32_t *rie = a.rank_in_expert + (size_t)t * a.k;
-            if ((a.k & 3) == 0) {
+            if (fused) {
+#pragma unroll
+                for (int j = 0; j < KMAX; ++j)
+                    if (j < a.k) store_agent(rie + j, r[j]);
+            } else if ((a.k & 3) == 0) {
 #pragma unroll
                 for (int j = 0; j < KMAX; j += 4)
                     if (j < a.k) *reinterpret_cast<int4 *>(rie + j) = make_int4(r[j], r[j + 1], r[j + 2], r[j + 3]);
@@ -421,7 +437,7 @@ __device__ __forceinline__ void layout_block(const LayoutArgs &a, int tile, int 
 
     if (fused) {
         // this block's ranks are readable by the dispatch waves from here on
-        __threadfence();
+        wait_own_stores();
         __syncthreads();
         if (tid == 0)
             __hip_atomic_store(a.rank_ready + (single ? replica : tile), epoch, __ATOMIC_RELAXED,
@@ -487,7 +503,7 @@ __device__ __forceinline__ void layout_block(const LayoutArgs &a, int tile, int 
         if (replica == 0) {
             for (int e = tid; e < a.E; e += kTileTokens) {
                 a.recv_cnt[e] = excl[e] + agg[e];
-                a.expert_off[e] = scan[e] - scan[rank_of(e, a.epr, a.epr_shift) * a.epr];
+                store_agent(a.expert_off + e, scan[e] - scan[rank_of(e, a.epr, a.epr_shift) * a.epr]);
             }
             for (int d = tid; d < a.R; d += kTileTokens) {
                 const int rows = scan[(d + 1) * a.epr] - scan[d * a.epr];
@@ -496,7 +512,7 @@ __device__ __forceinline__ void layout_block(const LayoutArgs &a, int tile, int 
             }
             if (fused) {
                 // expert offsets are readable by the dispatch waves from here on
-                __threadfence();
+                wait_own_stores();
                 __syncthreads();
                 if (tid == 0)
                     __hip_atomic_store(&a.counters[kTotalsReady], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
