@@ -23,6 +23,8 @@ struct ep_ctx {
     uint32_t *rank_ready;
     uint32_t spin_limit;
     bool debug;
+    int cu_count;
+    int fused_resident[2][2];  // [k > 8][fp8]: fused-kernel blocks the GPU holds at once (-1: not asked yet)
 };
 
 namespace {
@@ -314,10 +316,12 @@ int ep_create(const ep_config *cfg, ep_ctx **out) {
     ctx->debug = dbg && dbg[0] && dbg[0] != '0';
     const char *spin = std::getenv("EP_SPIN_LIMIT");
     ctx->spin_limit = spin ? (uint32_t)std::strtoul(spin, nullptr, 10) : (1u << 20);
-    if (hipGetDevice(&ctx->device) != hipSuccess) {
+    if (hipGetDevice(&ctx->device) != hipSuccess ||
+        hipDeviceGetAttribute(&ctx->cu_count, hipDeviceAttributeMultiprocessorCount, ctx->device) != hipSuccess) {
         delete ctx;
         return EP_ERR_HIP;
     }
+    for (auto &row : ctx->fused_resident) row[0] = row[1] = -1;
     if (hipMalloc(&ctx->ws, ctx->ws_bytes) != hipSuccess) {
         delete ctx;
         return EP_ERR_NOMEM;
@@ -394,7 +398,11 @@ int ep_dispatch_with_layout(ep_ctx *ctx, const uint16_t *x, const int32_t *topk_
     if (ctx->num_tiles == 1 && ep::inblock_lds_bytes(keys, c.num_topk) <= ep::kMaxBlockLds)
         return hip_fail(ep::launch_dispatch_inblock(la, da, use_fp8 != 0, g.num_waves, (hipStream_t)stream),
                         "ep_dispatch_with_layout");
-    return hip_fail(ep::launch_layout_dispatch(la, da, use_fp8 != 0, g.num_waves, (hipStream_t)stream),
+    int &resident = ctx->fused_resident[c.num_topk > 8][use_fp8 != 0];
+    if (resident < 0)
+        resident = ctx->cu_count * ep::layout_dispatch_blocks_per_cu(c.num_topk, use_fp8 != 0,
+                                                                     ep::layout_lds_bytes(keys));
+    return hip_fail(ep::launch_layout_dispatch(la, da, use_fp8 != 0, g.num_waves, resident, (hipStream_t)stream),
                     "ep_dispatch_with_layout");
 }
 

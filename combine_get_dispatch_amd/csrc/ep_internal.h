@@ -10,11 +10,11 @@ namespace ep {
 // Layout scan geometry: one workgroup of 256 threads (4 waves) handles 256
 // consecutive tokens, one token per lane; a single tile skips the cross-tile
 // machinery. LDS per key: 4 wave masks (8 B), 4 wave prefixes, the tile's
-// exclusive prefix and count (4 B each).
+// exclusive prefix and count, the expert scan (4 B each).
 constexpr int kLayoutTile = 256;
 constexpr int kCoResidentTiles = 256;  // grids up to this size number tiles by block index
 constexpr int kLayoutReplicas = 8;     // blocks sharing the outputs of a single tile
-inline size_t layout_lds_bytes(int keys) { return (size_t)keys * (4 * 8 + 4 * 4 + 2 * 4); }
+inline size_t layout_lds_bytes(int keys) { return (size_t)keys * (4 * 8 + 4 * 4 + 3 * 4); }
 // A fused launch on a single tile: every dispatch block builds the whole
 // layout in its own LDS and keeps each slot's (expert, rank) beside it.
 inline size_t inblock_lds_bytes(int keys, int k) { return layout_lds_bytes(keys) + (size_t)kLayoutTile * k * 4; }
@@ -76,8 +76,10 @@ hipError_t launch_dispatch(const DispatchArgs &a, bool fp8, bool forward, int nu
                            hipStream_t s);
 hipError_t launch_dispatch_inblock(const LayoutArgs &la, const DispatchArgs &da, bool fp8, int num_waves,
                                    hipStream_t s);
+// resident_blocks: blocks of the fused kernel the GPU holds at once (0: unknown)
 hipError_t launch_layout_dispatch(const LayoutArgs &la, const DispatchArgs &da, bool fp8, int num_waves,
-                                  hipStream_t s);
+                                  int resident_blocks, hipStream_t s);
+int layout_dispatch_blocks_per_cu(int k, bool fp8, size_t lds);
 hipError_t launch_combine(const CombineArgs &a, bool out_f32, int num_waves, hipStream_t s);
 hipError_t launch_copy(const void *src, void *dst, size_t n16, hipStream_t s);
 

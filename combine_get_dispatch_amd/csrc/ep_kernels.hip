@@ -156,7 +156,7 @@ struct LayoutLds {
     int32_t *wpre;    // [4][K] tokens in earlier waves
     int32_t *excl;    // [K] tokens in earlier tiles
     int32_t *agg;     // [K] tokens in this tile
-    int32_t *scan;    // last step only (aliases wpre): [E+1] prefix of expert rows
+    int32_t *scan;    // last tile: [E+1] prefix of expert rows (E + 1 <= K)
     int32_t *slots;   // in-block mode: [tile token][k] (expert << 16 | rank), -1 if not kept
 };
 
@@ -167,8 +167,8 @@ __device__ __forceinline__ LayoutLds layout_lds(int K) {
     v.wpre = reinterpret_cast<int32_t *>(lds + kTileWaves * K);
     v.excl = v.wpre + kTileWaves * K;
     v.agg = v.excl + K;
-    v.scan = v.wpre;
-    v.slots = v.agg + K;
+    v.scan = v.agg + K;
+    v.slots = v.scan + K;
     return v;
 }
 
@@ -382,7 +382,45 @@ __device__ __forceinline__ void layout_block(const LayoutArgs &a, int tile, int 
         }
     }
 
-    // 4. stable rank of each kept slot: tokens before it in earlier tiles,
+    // 4. the last tile holds every key's total (its look-back is done): rows
+    //    per expert, expert offsets inside each rank (block scan), rows per
+    //    rank. Replica 0 writes them, before its own ranks and per-source
+    //    counts, which nothing waits on as long; in-block copies keep the
+    //    scan to place their own slots.
+    if (last_tile && (replica == 0 || inblock)) {
+        const int chunk = (a.E + kTileTokens - 1) / kTileTokens;
+        const int lo = min(tid * chunk, a.E), hi = min(lo + chunk, a.E);
+        int local = 0;
+        for (int e = lo; e < hi; ++e) local += excl[e] + agg[e];
+        int total;
+        int run = block_exclusive_scan(local, s_part, &total);
+        for (int e = lo; e < hi; ++e) {
+            scan[e] = run;
+            run += excl[e] + agg[e];
+        }
+        if (tid == 0) scan[a.E] = total;
+        __syncthreads();
+        if (replica == 0) {
+            for (int e = tid; e < a.E; e += kTileTokens) {
+                a.recv_cnt[e] = excl[e] + agg[e];
+                store_agent(a.expert_off + e, scan[e] - scan[rank_of(e, a.epr, a.epr_shift) * a.epr]);
+            }
+            for (int d = tid; d < a.R; d += kTileTokens) {
+                const int rows = scan[(d + 1) * a.epr] - scan[d * a.epr];
+                a.rank_rows[d] = rows;
+                if ((int64_t)rows > a.cap_rows) atomicOr(&a.counters[kStatus], kStCap);
+            }
+            if (fused) {
+                // expert offsets are readable by the dispatch waves from here on
+                wait_own_stores();
+                __syncthreads();
+                if (tid == 0)
+                    __hip_atomic_store(&a.counters[kTotalsReady], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+    }
+
+    // 5. stable rank of each kept slot: tokens before it in earlier tiles,
     //    earlier waves of this tile, and earlier lanes of its wave (in-block:
     //    every token's, kept in LDS for the block's dispatch waves)
     int r[KMAX];
@@ -444,14 +482,14 @@ __device__ __forceinline__ void layout_block(const LayoutArgs &a, int tile, int 
                                __HIP_MEMORY_SCOPE_AGENT);
     }
 
-    // 5. per-source counts for the source ranks that end in this tile
+    // 6. per-source counts for the source ranks that end in this tile
     //    (source s = tokens [s*T/R, (s+1)*T/R)); a start boundary owned by an
     //    earlier tile is read back once that tile has published its prefixes
     if (!single && last_hi > last_lo) {
         const bool remote = last_lo * a.tpr < t0;  // only the first such source can start earlier
-        int32_t *remote_lo = wpre;                 // [K] its start prefixes (wpre is free after step 4)
+        int32_t *remote_lo = wpre;                 // [K] its start prefixes (wpre is free after step 5)
         if (remote) {
-            __syncthreads();  // every wave is past step 4
+            __syncthreads();  // every wave is past step 5
             if (tid == 0) {
                 const int owner = (last_lo * a.tpr) / kTileTokens;
                 uint32_t spins = 0;
@@ -479,43 +517,6 @@ __device__ __forceinline__ void layout_block(const LayoutArgs &a, int tile, int 
                     a.cnt_se[(size_t)s * a.E + key] = hi - lo;
                 else
                     a.cnt_sd[(size_t)s * a.R + (key - a.E)] = hi - lo;
-            }
-        }
-    }
-
-    // 6. the last tile holds every key's total: rows per expert, expert
-    //    offsets inside each rank (block scan), rows per rank. Replica 0
-    //    writes them; in-block copies keep the scan to place their own slots.
-    if (last_tile && (replica == 0 || inblock)) {
-        __syncthreads();  // wpre is reused as the scan array below
-        const int chunk = (a.E + kTileTokens - 1) / kTileTokens;
-        const int lo = min(tid * chunk, a.E), hi = min(lo + chunk, a.E);
-        int local = 0;
-        for (int e = lo; e < hi; ++e) local += excl[e] + agg[e];
-        int total;
-        int run = block_exclusive_scan(local, s_part, &total);
-        for (int e = lo; e < hi; ++e) {
-            scan[e] = run;
-            run += excl[e] + agg[e];
-        }
-        if (tid == 0) scan[a.E] = total;
-        __syncthreads();
-        if (replica == 0) {
-            for (int e = tid; e < a.E; e += kTileTokens) {
-                a.recv_cnt[e] = excl[e] + agg[e];
-                store_agent(a.expert_off + e, scan[e] - scan[rank_of(e, a.epr, a.epr_shift) * a.epr]);
-            }
-            for (int d = tid; d < a.R; d += kTileTokens) {
-                const int rows = scan[(d + 1) * a.epr] - scan[d * a.epr];
-                a.rank_rows[d] = rows;
-                if ((int64_t)rows > a.cap_rows) atomicOr(&a.counters[kStatus], kStCap);
-            }
-            if (fused) {
-                // expert offsets are readable by the dispatch waves from here on
-                wait_own_stores();
-                __syncthreads();
-                if (tid == 0)
-                    __hip_atomic_store(&a.counters[kTotalsReady], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
         }
     }
@@ -795,7 +796,8 @@ __global__ __launch_bounds__(kTileTokens) void k_dispatch_inblock(LayoutArgs la,
     const float wslot = (active && part == 0 && lane < da.k && da.recv_w) ? da.w[(size_t)t * da.k + lane] : 0.0f;
     u32x4 v[2 * kMaxPassPerWave];
     load_rows<FP8>(da, t, part, active, v);
-    layout_block<KMAX>(la, 0, (int)blockIdx.x, (int)gridDim.x, kLayoutInBlock, raw, 0u);  // ends at a barrier
+    layout_block<KMAX>(la, 0, (int)blockIdx.x, (int)gridDim.x, kLayoutInBlock, raw, 0u);
+    __syncthreads();  // the slots and the scan are in LDS
     if (!active) return;
     const int p = slot_row_lds(da, layout_lds(la.E + la.R), t, lane, part, wslot);
     store_rows<FP8>(da, part, p, v);
@@ -804,23 +806,39 @@ __global__ __launch_bounds__(kTileTokens) void k_dispatch_inblock(LayoutArgs la,
 // The dispatch side of a fused grid with flags: the block's NW waves load
 // (and, for FP8, later quantize) their rows before the layout is known, wait
 // for the layout blocks of their tokens and for the totals, then write the
-// rows. `db` is the block's index among the dispatch blocks.
+// rows. `db` is the block's index among the dispatch blocks, which take the
+// work items [0, items).
 template <bool FP8, int NW>
-__device__ __forceinline__ void fused_dispatch_block(const DispatchArgs &da, const LayoutWait &lw, int db) {
+__device__ __forceinline__ void fused_dispatch_block(const DispatchArgs &da, const LayoutWait &lw, int db, int items) {
     const int gw = db * NW + (int)(threadIdx.x >> 6);
     const int t = gw / da.waves_per_token;
     const int part = gw - t * da.waves_per_token;
-    const bool active = t < da.T;  // whole wave
+    const bool active = gw < items;  // whole wave
     u32x4 v[2 * kMaxPassPerWave];
     load_rows<FP8>(da, t, part, active, v);  // loaded before the layout is known
     // every wave of the block reaches the barrier inside
     const int gw0 = db * NW;
     const int t_first = min(gw0 / da.waves_per_token, da.T - 1);
-    const int t_last = min((gw0 + NW - 1) / da.waves_per_token, da.T - 1);
-    wait_for_layout(lw, t_first, t_last);
+    const int t_last = min((min(gw0 + NW, items) - 1) / da.waves_per_token, da.T - 1);
+    wait_for_layout(lw, t_first, max(t_last, t_first));
     if (active) {
         const int p = slot_row<true, true>(da, t, threadIdx.x & 63, part);
         store_rows<FP8>(da, part, p, v);
+    }
+}
+
+// One wave waits for the layout block that wrote token t's ranks and for
+// the totals (a layout wave taking a dispatch item after its layout work).
+__device__ __forceinline__ void wave_wait_for_layout(const LayoutWait &w, int t) {
+    const uint32_t *flag = w.rank_ready + t / w.tokens_per_block;
+    uint32_t spins = 0;
+    while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != w.epoch ||
+           __hip_atomic_load(w.totals_ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != w.epoch) {
+        if (++spins > w.spin_limit) {
+            atomicOr(w.status, kStTimeout);
+            break;
+        }
+        __builtin_amdgcn_s_sleep(2);
     }
 }
 
@@ -853,23 +871,44 @@ __device__ __forceinline__ void fused_rearm(const LayoutArgs &la) {
 // layout (the tiles, or the replicas of one tile), the rest are dispatch
 // waves that load and quantize their rows first and wait for the layout only
 // to place them. Layout blocks have the lowest indices, so they are running
-// before any dispatch block waits.
+// before any dispatch block waits. When the grid would not fit on the GPU at
+// once, the last `extra` work items (at most four per layout block) go to the
+// layout blocks' own waves once their layout work is done, so that no
+// dispatch block has to wait for a free slot (it would then run its chain of
+// dependent loads behind everyone's row traffic). Not with a ticket: then
+// the layout blocks themselves need the slots their predecessors free.
 template <int KMAX, bool FP8>
-__global__ __launch_bounds__(kTileTokens) void k_layout_dispatch(LayoutArgs la, DispatchArgs da, int lgrid) {
+__global__ __launch_bounds__(kTileTokens) void k_layout_dispatch(LayoutArgs la, DispatchArgs da, int lgrid,
+                                                                 int extra) {
     const int b = (int)blockIdx.x;
+    const int items = da.T * da.waves_per_token;
+    const int tpb = la.num_tiles > 1 ? kTileTokens : (la.T + lgrid - 1) / lgrid;
     if (b < lgrid) {
         int replica, nrep;
         const int tile = layout_tile_of_block(la, b, lgrid, &replica, &nrep);
+        uint32_t epoch = 0;
         if (tile >= 0) {
             int raw[KMAX];
             load_slots<KMAX>(la, tile * kTileTokens + (int)threadIdx.x, raw);
-            const uint32_t epoch = load_epoch(la);
+            epoch = load_epoch(la);
             layout_block<KMAX>(la, tile, replica, nrep, kLayoutFlags, raw, epoch);
+        } else {
+            epoch = load_epoch(la);
+        }
+        const int lw = b * kWavesPerBlock + (int)(threadIdx.x >> 6);
+        const int gw = items - extra + lw;
+        const int t = gw / da.waves_per_token;
+        if (lw < extra) {  // whole wave
+            const int part = gw - t * da.waves_per_token;
+            u32x4 v[2 * kMaxPassPerWave];
+            load_rows<FP8>(da, t, part, true, v);
+            wave_wait_for_layout(make_wait(la, epoch, tpb), t);
+            const int p = slot_row<true, true>(da, t, threadIdx.x & 63, part);
+            store_rows<FP8>(da, part, p, v);
         }
     } else {
         const uint32_t epoch = load_epoch(la);
-        const int tpb = la.num_tiles > 1 ? kTileTokens : (la.T + lgrid - 1) / lgrid;
-        fused_dispatch_block<FP8, kWavesPerBlock>(da, make_wait(la, epoch, tpb), b - lgrid);
+        fused_dispatch_block<FP8, kWavesPerBlock>(da, make_wait(la, epoch, tpb), b - lgrid, items - extra);
     }
     fused_rearm(la);
 }
@@ -1012,22 +1051,40 @@ hipError_t launch_layout(const LayoutArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
+const void *layout_dispatch_fn(int k, bool fp8) {
+    if (k <= 8) return fp8 ? (const void *)k_layout_dispatch<8, true> : (const void *)k_layout_dispatch<8, false>;
+    return fp8 ? (const void *)k_layout_dispatch<kMaxTopk, true> : (const void *)k_layout_dispatch<kMaxTopk, false>;
+}
+
+int layout_dispatch_blocks_per_cu(int k, bool fp8, size_t lds) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, layout_dispatch_fn(k, fp8), kTileTokens, lds) != hipSuccess)
+        return 0;
+    return n;
+}
+
 hipError_t launch_layout_dispatch(const LayoutArgs &la, const DispatchArgs &da, bool fp8, int num_waves,
-                                  hipStream_t s) {
+                                  int resident_blocks, hipStream_t s) {
     const size_t lds = layout_lds_bytes(la.E + la.R);
     const int lgrid = la.num_tiles > 1 ? la.num_tiles : max(1, min(la.R, kLayoutReplicas));
-    const int grid = lgrid + (num_waves + kWavesPerBlock - 1) / kWavesPerBlock;
+    // items the layout blocks' waves take: the overflow of a grid that would
+    // not be resident at once, if the layout blocks all are
+    int extra = 0;
+    const int full = lgrid + (num_waves + kWavesPerBlock - 1) / kWavesPerBlock;
+    if (!la.use_ticket && resident_blocks > 0 && full > resident_blocks)
+        extra = min(num_waves, min(lgrid, full - resident_blocks) * kWavesPerBlock);
+    const int grid = lgrid + (num_waves - extra + kWavesPerBlock - 1) / kWavesPerBlock;
     const dim3 block(kTileTokens);
     if (la.k <= 8) {
         if (fp8)
-            hipLaunchKernelGGL((k_layout_dispatch<8, true>), dim3(grid), block, lds, s, la, da, lgrid);
+            hipLaunchKernelGGL((k_layout_dispatch<8, true>), dim3(grid), block, lds, s, la, da, lgrid, extra);
         else
-            hipLaunchKernelGGL((k_layout_dispatch<8, false>), dim3(grid), block, lds, s, la, da, lgrid);
+            hipLaunchKernelGGL((k_layout_dispatch<8, false>), dim3(grid), block, lds, s, la, da, lgrid, extra);
     } else {
         if (fp8)
-            hipLaunchKernelGGL((k_layout_dispatch<kMaxTopk, true>), dim3(grid), block, lds, s, la, da, lgrid);
+            hipLaunchKernelGGL((k_layout_dispatch<kMaxTopk, true>), dim3(grid), block, lds, s, la, da, lgrid, extra);
         else
-            hipLaunchKernelGGL((k_layout_dispatch<kMaxTopk, false>), dim3(grid), block, lds, s, la, da, lgrid);
+            hipLaunchKernelGGL((k_layout_dispatch<kMaxTopk, false>), dim3(grid), block, lds, s, la, da, lgrid, extra);
     }
     return hipGetLastError();
 }
