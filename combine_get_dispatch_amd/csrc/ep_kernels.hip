@@ -190,6 +190,112 @@ __device__ __forceinline__ uint32_t load_epoch(const LayoutArgs &a) {
     return __hip_atomic_load(&a.counters[kEpoch], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// One key's count in each wave of the tile and in the tile (LDS), published
+// for the look-back of later tiles (tile 0's count is its inclusive prefix).
+__device__ __forceinline__ void tile_counts(const uint64_t *masks, int32_t *wpre, int32_t *agg, const LayoutArgs &a,
+                                            int K, int key, int tile, uint32_t epoch, bool single) {
+    const int c0 = __popcll(masks[key]), c1 = __popcll(masks[K + key]), c2 = __popcll(masks[2 * K + key]),
+              c3 = __popcll(masks[3 * K + key]);
+    wpre[key] = 0;
+    wpre[K + key] = c0;
+    wpre[2 * K + key] = c0 + c1;
+    wpre[3 * K + key] = c0 + c1 + c2;
+    const int c = c0 + c1 + c2 + c3;
+    agg[key] = c;
+    if (!single)
+        __hip_atomic_store(a.tile_state + (size_t)tile * K + key,
+                           pack_state(epoch, tile == 0 ? kFlagPrefix : kFlagAgg, (uint32_t)c), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// What one tile's per-key look-back needs (registers and LDS of layout_block).
+struct TileView {
+    const LayoutArgs &a;
+    const uint64_t *masks;
+    const int32_t *agg;
+    int32_t *excl;
+    int K, tile;
+    uint32_t epoch;
+    bool single;
+    int replica, nrep, t0, ntile, first_lo, first_hi;
+    bool publish;
+};
+
+// Decoupled look-back of one key, a window of predecessors per round trip:
+// add counts from the nearest predecessor back to the first inclusive
+// prefix; a predecessor that has not published yet ends the window and is
+// read again. Then this tile's share of the key's per-source outputs:
+// prefixes at the source-rank boundaries it owns (boundary s = token s*T/R):
+// src_expert_off directly, and a copy for later tiles. The tile's stores
+// come after its look-back loads (stores and loads share one in-order
+// completion counter).
+__device__ __forceinline__ void lookback_key(const TileView &v, int key) {
+    const LayoutArgs &a = v.a;
+    const int K = v.K;
+    int sum = 0;
+    if (!v.single && v.tile > 0) {
+        int hi = v.tile - 1;
+        uint32_t spins = 0;
+        while (hi >= 0) {
+            uint64_t sv[kLookbackWindow];
+#pragma unroll
+            for (int i = 0; i < kLookbackWindow; ++i)
+                sv[i] = (hi - i >= 0) ? __hip_atomic_load(a.tile_state + (size_t)(hi - i) * K + key,
+                                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                      : 0ull;
+            int consumed = 0;
+            bool found = false, stall = false;
+#pragma unroll
+            for (int i = 0; i < kLookbackWindow; ++i) {
+                if (found || stall || hi - i < 0) continue;
+                const uint32_t fl = (uint32_t)(sv[i] >> 32) & 3u;
+                if ((uint32_t)(sv[i] >> 34) != v.epoch || fl == 0) {
+                    stall = true;
+                    continue;
+                }
+                sum += (int32_t)(uint32_t)sv[i];
+                ++consumed;
+                if (fl == kFlagPrefix) found = true;
+            }
+            if (found) break;
+            hi -= consumed;
+            if (stall) {
+                if (++spins > a.spin_limit) {
+                    atomicOr(&a.counters[kStatus], kStTimeout);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+        }
+        __hip_atomic_store(a.tile_state + (size_t)v.tile * K + key,
+                           pack_state(v.epoch, kFlagPrefix, (uint32_t)(sum + v.agg[key])), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+    v.excl[key] = sum;
+    const bool is_expert = key < a.E;
+    const KeyView kv = key_view(v.masks, K, key);
+    if (v.single) {
+        // every boundary is here: per-source counts and offsets at once,
+        // the replicas taking the source ranks in turn
+        for (int s = v.replica; s < a.R; s += v.nrep) {
+            const int lo = count_before(kv, s * a.tpr, v.ntile);
+            const int hi = count_before(kv, (s + 1) * a.tpr, v.ntile);
+            if (is_expert) {
+                a.cnt_se[(size_t)s * a.E + key] = hi - lo;
+                a.src_expert_off[(size_t)s * a.E + key] = lo;
+            } else {
+                a.cnt_sd[(size_t)s * a.R + (key - a.E)] = hi - lo;
+            }
+        }
+    } else {
+        for (int s = v.first_lo; s < v.first_hi; ++s) {
+            const int pre = sum + count_before(kv, s * a.tpr - v.t0, v.ntile);
+            if (is_expert) a.src_expert_off[(size_t)s * a.E + key] = pre;
+            if (v.publish && s == v.first_hi - 1) a.bp[(size_t)s * K + key] = pre;
+        }
+    }
+}
+
 // The layout of tile `tile` (its 256 tokens are t0 + thread), given the
 // thread's slots `raw` and the call's epoch. A single tile may run as `nrep`
 // replicas that split the outputs (replica = this copy); several tiles chain
@@ -234,8 +340,11 @@ __device__ __forceinline__ void layout_block(const LayoutArgs &a, int tile, int 
     for (int i = lane; i < K; i += 64) masks[wave * K + i] = 0;
 
     // 1. validate the token's slots; expert bits go into the wave's masks
-    //    (LDS atomics), the per-rank bits are wave ballots (no atomics: every
-    //    lane would hit the same few words)
+    //    (LDS atomics); the token's ranks go into a register mask. One tile:
+    //    the per-rank LDS masks are wave ballots of it (no atomics: every
+    //    lane would hit the same few words). Several tiles: they are the ORs
+    //    of their experts' masks, built in step 6, off the path to the ranks
+    //    and the totals.
     int ev[KMAX];
     uint32_t st = 0;
     uint64_t rmask = 0;
@@ -259,7 +368,7 @@ __device__ __forceinline__ void layout_block(const LayoutArgs &a, int tile, int 
         atomicOr(reinterpret_cast<unsigned long long *>(&masks[wave * K + v]), (unsigned long long)bit);
         rmask |= 1ull << rank_of(v, a.epr, a.epr_shift);
     }
-    {
+    if (single) {
         uint64_t mine = 0;
         for (int d = 0; d < a.R; ++d) {
             const uint64_t b = __ballot((rmask >> d) & 1);
@@ -273,114 +382,19 @@ __device__ __forceinline__ void layout_block(const LayoutArgs &a, int tile, int 
     if (st && replica == 0) atomicOr(&a.counters[kStatus], st);
     __syncthreads();
 
-    // 2. per key: tokens in earlier waves and the tile's count; published at
-    //    once for the look-back (tile 0's count is already its inclusive prefix)
-    for (int key = tid; key < K; key += kTileTokens) {
-        const int c0 = __popcll(masks[key]), c1 = __popcll(masks[K + key]), c2 = __popcll(masks[2 * K + key]),
-                  c3 = __popcll(masks[3 * K + key]);
-        wpre[key] = 0;
-        wpre[K + key] = c0;
-        wpre[2 * K + key] = c0 + c1;
-        wpre[3 * K + key] = c0 + c1 + c2;
-        const int c = c0 + c1 + c2 + c3;
-        agg[key] = c;
-        if (!single)
-            __hip_atomic_store(a.tile_state + (size_t)tile * K + key,
-                               pack_state(epoch, tile == 0 ? kFlagPrefix : kFlagAgg, (uint32_t)c),
-                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    // 2. per expert key: tokens in earlier waves and the tile's count;
+    //    published at once for the look-back (tile 0's count is already its
+    //    inclusive prefix)
+    for (int key = tid; key < a.E; key += kTileTokens) tile_counts(masks, wpre, agg, a, K, key, tile, epoch, single);
 
-    // 3. decoupled look-back, a window of predecessors per round trip: add
-    //    counts from the nearest predecessor back to the first inclusive
-    //    prefix; a predecessor that has not published yet ends the window and
-    //    is read again. Then this tile's share of the per-source outputs:
-    //    prefixes at the source-rank boundaries it owns (boundary s = token
-    //    s*T/R): src_expert_off directly, and a copy for later tiles. The
-    //    tile's stores come after its look-back loads (stores and loads share
-    //    one in-order completion counter).
-    for (int key = tid; key < K; key += kTileTokens) {
-        int sum = 0;
-        if (!single && tile > 0) {
-            int hi = tile - 1;
-            uint32_t spins = 0;
-            while (hi >= 0) {
-                uint64_t sv[kLookbackWindow];
-#pragma unroll
-                for (int i = 0; i < kLookbackWindow; ++i)
-                    sv[i] = (hi - i >= 0) ? __hip_atomic_load(a.tile_state + (size_t)(hi - i) * K + key,
-                                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                                          : 0ull;
-                int consumed = 0;
-                bool found = false, stall = false;
-#pragma unroll
-                for (int i = 0; i < kLookbackWindow; ++i) {
-                    if (found || stall || hi - i < 0) continue;
-                    const uint32_t fl = (uint32_t)(sv[i] >> 32) & 3u;
-                    if ((uint32_t)(sv[i] >> 34) != epoch || fl == 0) {
-                        stall = true;
-                        continue;
-                    }
-                    sum += (int32_t)(uint32_t)sv[i];
-                    ++consumed;
-                    if (fl == kFlagPrefix) found = true;
-                }
-                if (found) break;
-                hi -= consumed;
-                if (stall) {
-                    if (++spins > a.spin_limit) {
-                        atomicOr(&a.counters[kStatus], kStTimeout);
-                        break;
-                    }
-                    __builtin_amdgcn_s_sleep(1);
-                }
-            }
-            __hip_atomic_store(a.tile_state + (size_t)tile * K + key,
-                               pack_state(epoch, kFlagPrefix, (uint32_t)(sum + agg[key])), __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-        }
-        excl[key] = sum;
-        const bool is_expert = key < a.E;
-        const KeyView kv = key_view(masks, K, key);
-        if (single) {
-            // every boundary is here: per-source counts and offsets at once,
-            // the replicas taking the source ranks in turn
-            for (int s = replica; s < a.R; s += nrep) {
-                const int lo = count_before(kv, s * a.tpr, ntile);
-                const int hi = count_before(kv, (s + 1) * a.tpr, ntile);
-                if (is_expert) {
-                    a.cnt_se[(size_t)s * a.E + key] = hi - lo;
-                    a.src_expert_off[(size_t)s * a.E + key] = lo;
-                } else {
-                    a.cnt_sd[(size_t)s * a.R + (key - a.E)] = hi - lo;
-                }
-            }
-        } else {
-            for (int s = first_lo; s < first_hi; ++s) {
-                const int pre = sum + count_before(kv, s * a.tpr - t0, ntile);
-                if (is_expert) a.src_expert_off[(size_t)s * a.E + key] = pre;
-                if (publish && s == first_hi - 1) a.bp[(size_t)s * K + key] = pre;
-            }
-        }
-    }
-    if (publish) __threadfence();  // every wave's prefix stores complete before the flag
+    // 3. decoupled look-back of the expert keys (the ranks and the totals
+    //    wait on them); the rank keys, which only the per-source counts
+    //    need, follow the ranks (step 6) so that no thread runs two chains
+    //    before the totals.
+    const TileView tv{a, masks, agg, excl, K, tile, epoch, single, replica, nrep, t0, ntile,
+                      first_lo, first_hi, publish};
+    for (int key = tid; key < a.E; key += kTileTokens) lookback_key(tv, key);
     __syncthreads();
-    if (!single && tid == 0) {
-        if (publish) {
-            // the start prefixes of the source that ends in a later tile are
-            // visible from here on
-            __hip_atomic_store(a.bp_ready + tile, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        // Re-arm the workspace for the next call once every tile has read
-        // the epoch: the last tile's look-back has (transitively) seen every
-        // tile's count, and a tile publishes only after reading the epoch.
-        // (Fused grids re-arm when their last block ends.)
-        if (!fused && last_tile) {
-            uint32_t ne = (epoch + 1u) & ((1u << 30) - 1u);
-            if (ne == 0) ne = 1;
-            __hip_atomic_store(&a.counters[kTicket], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&a.counters[kEpoch], ne, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-    }
 
     // 4. the last tile holds every key's total (its look-back is done): rows
     //    per expert, expert offsets inside each rank (block scan), rows per
@@ -482,7 +496,37 @@ __device__ __forceinline__ void layout_block(const LayoutArgs &a, int tile, int 
                                __HIP_MEMORY_SCOPE_AGENT);
     }
 
-    // 6. per-source counts for the source ranks that end in this tile
+    // 6. the rank keys: masks (a token is on rank d if one of its kept slots'
+    //    experts is), counts, look-back; the boundary prefixes of a source that
+    //    ends in a later tile are published once both kinds of keys have
+    //    theirs; the workspace is re-armed once the last tile has seen every
+    //    tile's counts (a tile publishes only after reading the epoch; fused
+    //    grids re-arm when their last block ends)
+    if (!single) {
+        for (int i = tid; i < kTileWaves * a.R; i += kTileTokens) {
+            const int w = i / a.R, d = i - w * a.R;
+            uint64_t m = 0;
+            for (int e = d * a.epr; e < (d + 1) * a.epr; ++e) m |= masks[w * K + e];
+            masks[w * K + a.E + d] = m;
+        }
+        __syncthreads();
+        for (int key = a.E + tid; key < K; key += kTileTokens)
+            tile_counts(masks, wpre, agg, a, K, key, tile, epoch, single);
+    }
+    for (int key = a.E + tid; key < K; key += kTileTokens) lookback_key(tv, key);
+    if (publish) __threadfence();  // every wave's prefix stores complete before the flag
+    __syncthreads();
+    if (!single && tid == 0) {
+        if (publish) __hip_atomic_store(a.bp_ready + tile, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (!fused && last_tile) {
+            uint32_t ne = (epoch + 1u) & ((1u << 30) - 1u);
+            if (ne == 0) ne = 1;
+            __hip_atomic_store(&a.counters[kTicket], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&a.counters[kEpoch], ne, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+
+    // 7. per-source counts for the source ranks that end in this tile
     //    (source s = tokens [s*T/R, (s+1)*T/R)); a start boundary owned by an
     //    earlier tile is read back once that tile has published its prefixes
     if (!single && last_hi > last_lo) {
