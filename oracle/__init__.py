@@ -66,6 +66,12 @@ def _bind(lib):
     lib.oracle_combine.argtypes = [i, i, i, P, P, P, P, i, P, P]
     lib.oracle_combine_backward.restype = None
     lib.oracle_combine_backward.argtypes = [i, i, i, P, P, P]
+    lib.oracle_layout_dedup.restype = ctypes.c_uint32
+    lib.oracle_layout_dedup.argtypes = [i, i, i, i, ll, P, P, P]
+    lib.oracle_positions_dedup.restype = None
+    lib.oracle_positions_dedup.argtypes = [i, i, i, i, ll, P, P, P, P]
+    lib.oracle_dispatch_dedup.restype = None
+    lib.oracle_dispatch_dedup.argtypes = [i, i, i, i, i, i, P, P, P, P, P, i, P, P, P, P]
     for name in ("oracle_e4m3_encode", "oracle_e4m3_decode", "oracle_bf16_round"):
         getattr(lib, name).restype = None
         getattr(lib, name).argtypes = [P, P, ll]
@@ -233,6 +239,48 @@ class Oracle:
     def dispatch_backward(self, grad_rows: np.ndarray, pos: np.ndarray,
                           w: Optional[np.ndarray], tokens: Optional[np.ndarray] = None):
         return self.combine(grad_rows, pos, w, tokens=tokens)
+
+    # -- the rank-deduplicated exchange ------------------------------------
+    def layout_dedup(self, topk_idx: np.ndarray, E: int, R: int, cap_rows: int):
+        """Returns (rank_in_rank [T,k] int32, token_rows [R] int32, status)."""
+        topk_idx = _c(topk_idx, np.int32)
+        T, k = topk_idx.shape
+        assert E % R == 0 and T % R == 0
+        rir = np.empty((T, k), np.int32)
+        rows = np.zeros(R, np.int32)
+        st = int(self.lib.oracle_layout_dedup(T, k, E, R, int(cap_rows), _ptr(topk_idx), _ptr(rir), _ptr(rows)))
+        return rir, rows, st
+
+    def positions_dedup(self, topk_idx: np.ndarray, rank_in_rank: np.ndarray, E: int, R: int, cap_rows: int):
+        """Returns (pos [T,k] int32, src_idx [R*cap_rows] int32, -1 where unused)."""
+        topk_idx = _c(topk_idx, np.int32)
+        T, k = topk_idx.shape
+        pos = np.empty((T, k), np.int32)
+        src_idx = np.full(R * int(cap_rows), -1, np.int32)
+        self.lib.oracle_positions_dedup(T, k, E, R, int(cap_rows), _ptr(topk_idx),
+                                        _ptr(_c(rank_in_rank, np.int32)), _ptr(pos), _ptr(src_idx))
+        return pos, src_idx
+
+    def dispatch_dedup(self, x: np.ndarray, topk_idx: np.ndarray, topk_w: Optional[np.ndarray],
+                       pos: np.ndarray, E: int, R: int, num_rows: int, use_fp8: bool,
+                       tokens: Optional[np.ndarray] = None):
+        """Returns (recv_x, recv_scales or None, recv_topk_idx, recv_topk_w); rows
+        no slot maps to stay 0 (recv_topk_idx -1)."""
+        x = _c(x, np.uint16)
+        topk_idx = _c(topk_idx, np.int32)
+        T, H = x.shape
+        k = topk_idx.shape[1]
+        G = H // 128
+        recv_x = np.zeros((num_rows, H), np.uint8 if use_fp8 else np.uint16)
+        recv_scales = np.zeros((num_rows, G), np.float32) if use_fp8 else None
+        rti = np.full((num_rows, k), -1, np.int32)
+        rtw = np.zeros((num_rows, k), np.float32)
+        tw = None if topk_w is None else _c(topk_w, np.float32)
+        tk = None if tokens is None else _c(tokens, np.int32)
+        self.lib.oracle_dispatch_dedup(T, k, H, E, R, int(bool(use_fp8)), _ptr(x), _ptr(topk_idx), _ptr(tw),
+                                       _ptr(_c(pos, np.int32)), _ptr(tk), 0 if tk is None else tk.size,
+                                       _ptr(recv_x), _ptr(recv_scales), _ptr(rti), _ptr(rtw))
+        return recv_x, recv_scales, rti, rtw
 
     def forward(self, x, topk_idx, topk_w, E: int, R: int, cap_rows: int, use_fp8: bool):
         """Layout + positions + dispatch, as one convenience call for tests."""

@@ -266,6 +266,116 @@ void oracle_positions(int T, int k, int E, int R, long long cap_rows,
     }
 }
 
+/* ------------------------------------------------------------------------- */
+/* Rank-deduplicated exchange: one received row per (token, destination rank)
+ * instead of one per (token, expert). Reading (the pages' normal kernels send
+ * a token once per rank; the row then carries which of that rank's experts
+ * take it): the first valid slot of token t whose expert lives on rank d is
+ * the pair's "leader" slot, and rank d's rows hold its tokens in source-token
+ * order (the same stable order as the per-expert rows). */
+
+/* rank_in_rank[t][j] = number of tokens t' < t that have a valid slot on rank
+ * d(e) where e = topk_idx[t][j], if slot j is the leader of (t, d); -1 for
+ * every other slot. token_rows[d] = tokens with a valid slot on rank d.
+ * Returns the validation status bits and 4 if some token_rows[d] > cap_rows. */
+uint32_t oracle_layout_dedup(int T, int k, int E, int R, long long cap_rows,
+                             const int32_t *topk_idx, int32_t *rank_in_rank, int32_t *token_rows) {
+    uint32_t status = 0;
+    int experts_per_rank = E / R;
+    int32_t *fill = (int32_t *)calloc((size_t)R, sizeof(int32_t));
+    for (int t = 0; t < T; ++t) {
+        const int32_t *row = topk_idx + (size_t)t * k;
+        for (int j = 0; j < k; ++j) {
+            rank_in_rank[(size_t)t * k + j] = -1;
+            if (!slot_is_valid(row, j, E, &status)) continue;
+            int d = row[j] / experts_per_rank;
+            int leader = 1;
+            for (int jj = 0; jj < j; ++jj) {
+                uint32_t ignore = 0;
+                if (slot_is_valid(row, jj, E, &ignore) && row[jj] / experts_per_rank == d) leader = 0;
+            }
+            if (!leader) continue;
+            rank_in_rank[(size_t)t * k + j] = fill[d];
+            fill[d] += 1;
+        }
+    }
+    for (int d = 0; d < R; ++d) {
+        token_rows[d] = fill[d];
+        if ((long long)fill[d] > cap_rows) status |= ORACLE_ST_CAPACITY;
+    }
+    free(fill);
+    return status;
+}
+
+/* Handle of the deduplicated exchange: for a leader slot (t, j) of rank d,
+ * pos[t][j] = d * cap_rows + rank_in_rank[t][j] (-1 if that reaches cap_rows);
+ * -1 for every other slot. src_idx[pos] = t for every kept row. */
+void oracle_positions_dedup(int T, int k, int E, int R, long long cap_rows,
+                            const int32_t *topk_idx, const int32_t *rank_in_rank,
+                            int32_t *pos, int32_t *src_idx) {
+    int experts_per_rank = E / R;
+    for (int t = 0; t < T; ++t) {
+        for (int j = 0; j < k; ++j) {
+            size_t i = (size_t)t * k + j;
+            int32_t r = rank_in_rank[i];
+            if (r < 0 || (long long)r >= cap_rows) {
+                pos[i] = -1;
+                continue;
+            }
+            long long p = (long long)(topk_idx[i] / experts_per_rank) * cap_rows + r;
+            pos[i] = (int32_t)p;
+            src_idx[p] = t;
+        }
+    }
+}
+
+/* Deduplicated dispatch: each kept row p = pos[t][j] (leader of rank d)
+ * receives token t's row once (bit copy, or FP8 with the per-group scales as
+ * in oracle_dispatch), and k routing entries: for every slot j' of t,
+ *   recv_topk_idx[p][j'] = e' - d * E/R  and  recv_topk_w[p][j'] = topk_w[t][j']
+ * if slot j' is valid and its expert e' lives on rank d, else -1 and 0.0f.
+ * recv_topk_w is skipped if it or topk_w is NULL. tokens/ntokens restricts the
+ * work to a list of tokens (NULL = all T). */
+void oracle_dispatch_dedup(int T, int k, int H, int E, int R, int use_fp8, const uint16_t *x,
+                           const int32_t *topk_idx, const float *topk_w, const int32_t *pos,
+                           const int32_t *tokens, int ntokens, void *recv_x, float *recv_scales,
+                           int32_t *recv_topk_idx, float *recv_topk_w) {
+    int G = H / 128;
+    int experts_per_rank = E / R;
+    int n = tokens ? ntokens : T;
+    uint8_t *q = NULL;
+    float *sc = NULL;
+    if (use_fp8) {
+        q = (uint8_t *)malloc((size_t)H);
+        sc = (float *)malloc(sizeof(float) * (size_t)(G > 0 ? G : 1));
+    }
+    for (int ii = 0; ii < n; ++ii) {
+        int t = tokens ? tokens[ii] : ii;
+        const uint16_t *xr = x + (size_t)t * H;
+        const int32_t *row = topk_idx + (size_t)t * k;
+        if (use_fp8) oracle_quantize_token(H, xr, q, sc);
+        for (int j = 0; j < k; ++j) {
+            int32_t p = pos[(size_t)t * k + j];
+            if (p < 0) continue;
+            int d = row[j] / experts_per_rank;
+            if (use_fp8) {
+                memcpy((uint8_t *)recv_x + (size_t)p * H, q, (size_t)H);
+                memcpy(recv_scales + (size_t)p * G, sc, sizeof(float) * (size_t)G);
+            } else {
+                memcpy((uint16_t *)recv_x + (size_t)p * H, xr, sizeof(uint16_t) * (size_t)H);
+            }
+            for (int jj = 0; jj < k; ++jj) {
+                uint32_t ignore = 0;
+                int here = slot_is_valid(row, jj, E, &ignore) && row[jj] / experts_per_rank == d;
+                recv_topk_idx[(size_t)p * k + jj] = here ? row[jj] - d * experts_per_rank : -1;
+                if (recv_topk_w && topk_w) recv_topk_w[(size_t)p * k + jj] = here ? topk_w[(size_t)t * k + jj] : 0.0f;
+            }
+        }
+    }
+    free(q);
+    free(sc);
+}
+
 /* Per-token FP8 quantization, one scale per group of 128 channels.
  * Reading (the pages say only "FP8 dispatch"): for group g,
  *   amax  = max over the group of |x|                (exact)

@@ -40,6 +40,18 @@ void oracle_dispatch(int T, int k, int H, int use_fp8, const uint16_t *x,
 
 void oracle_quantize_token(int H, const uint16_t *x_row, uint8_t *q, float *scales);
 
+uint32_t oracle_layout_dedup(int T, int k, int E, int R, long long cap_rows,
+                             const int32_t *topk_idx, int32_t *rank_in_rank, int32_t *token_rows);
+
+void oracle_positions_dedup(int T, int k, int E, int R, long long cap_rows,
+                            const int32_t *topk_idx, const int32_t *rank_in_rank,
+                            int32_t *pos, int32_t *src_idx);
+
+void oracle_dispatch_dedup(int T, int k, int H, int E, int R, int use_fp8, const uint16_t *x,
+                           const int32_t *topk_idx, const float *topk_w, const int32_t *pos,
+                           const int32_t *tokens, int ntokens, void *recv_x, float *recv_scales,
+                           int32_t *recv_topk_idx, float *recv_topk_w);
+
 void oracle_combine(int T, int k, int H, const uint16_t *rows, const int32_t *pos,
                     const float *w, const int32_t *tokens, int ntokens,
                     uint16_t *y, float *acc);

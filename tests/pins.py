@@ -538,9 +538,152 @@ def pin_backward(orc):
     assert np.array_equal(gx, orc.combine(G, pos, w))
 
 
+# ---------------------------------------------------------------------------
+# rank-deduplicated exchange
+# ---------------------------------------------------------------------------
+
+def pin_dedup_golden(orc):
+    g = golden("layout_by_hand.json")
+    topk = np.array(g["topk_idx"], np.int32)
+    E, R, H = g["E"], g["R"], g["H"]
+    dd = g["dedup"]
+    w = np.tile(np.array([0.5, 0.25], np.float32), (topk.shape[0], 1))
+    x = bf16_bits_of(np.arange(topk.shape[0] * H, dtype=np.float32).reshape(-1, H))
+    for case in dd["cases"]:
+        cap = case["cap_rows"]
+        rir, rows, st = orc.layout_dedup(topk, E, R, cap)
+        assert np.array_equal(rir, np.array(dd["rank_in_rank"])), rir
+        assert np.array_equal(rows, np.array(dd["token_rows"])), rows
+        assert st == case["status"], (st, case["status"])
+        pos, src_idx = orc.positions_dedup(topk, rir, E, R, cap)
+        assert np.array_equal(pos, np.array(case["pos"])), ("pos", cap, pos)
+        if "recv_topk_idx" in case:
+            rx, _, rti, rtw = orc.dispatch_dedup(x, topk, w, pos, E, R, R * cap, use_fp8=False)
+            for row, want in case["recv_topk_idx"].items():
+                r = int(row)
+                assert np.array_equal(rti[r], np.array(want)), (r, rti[r], want)
+                assert np.array_equal(rtw[r], np.where(np.array(want) >= 0, w[src_idx[r]], 0.0)), r
+                assert np.array_equal(rx[r], x[src_idx[r]]), r
+
+
+def brute_dedup(topk, E, R):
+    """Leaders and per-rank rows counted directly from the definitions, O(T^2 k)."""
+    T, k = topk.shape
+    epr = E // R
+
+    def kept(t):  # valid slots of token t, first occurrence only
+        seen, out = set(), []
+        for j in range(k):
+            e = int(topk[t, j])
+            if 0 <= e < E and e not in seen:
+                out.append((j, e))
+            if 0 <= e < E:
+                seen.add(e)
+        return out
+
+    on = np.zeros((T, R), bool)
+    for t in range(T):
+        for _, e in kept(t):
+            on[t, e // epr] = True
+    rir = np.full((T, k), -1, np.int32)
+    for t in range(T):
+        done = set()
+        for j, e in kept(t):
+            d = e // epr
+            if d in done:
+                continue
+            done.add(d)
+            rir[t, j] = int(on[:t, d].sum())
+    return rir, on.sum(0).astype(np.int32), on
+
+
+def pin_dedup_bruteforce(orc):
+    rng = np.random.default_rng(57)
+    for T, k, E, R in ((32, 4, 16, 4), (40, 6, 24, 8), (24, 8, 8, 2)):
+        topk = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32)
+        topk[rng.random((T, k)) < 0.15] = -1
+        topk[rng.random((T, k)) < 0.05] = E + 3                          # bad ids
+        dup = rng.random(T) < 0.2
+        topk[dup, k - 1] = topk[dup, 0]                                   # repeats
+        rir, rows, _ = orc.layout_dedup(topk, E, R, 1 << 30)
+        brir, brows, on = brute_dedup(topk, E, R)
+        assert np.array_equal(rir, brir), (T, k, E, R)
+        assert np.array_equal(rows, brows)
+        L = orc.layout(topk, E, R, 1 << 30)
+        assert np.array_equal(rows, L.cnt_sd.sum(0)), "token rows != summed cnt_sd"
+        assert np.array_equal(on.astype(np.uint8), L.is_token_in_rank)
+        assert ((rir >= 0).sum(1) == L.is_token_in_rank.sum(1)).all(), "one leader per (token, rank)"
+
+
+def pin_dedup_dispatch(orc):
+    rng = np.random.default_rng(58)
+    T, k, E, R, H = 32, 4, 16, 4, 256
+    topk = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32)
+    topk[rng.random((T, k)) < 0.1] = -1
+    w = rng.random((T, k)).astype(np.float32)
+    x = bf16_bits_of(rng.standard_normal((T, H)).astype(np.float32))
+    rir, rows, _ = orc.layout_dedup(topk, E, R, 1 << 30)
+    cap = int(rows.max())
+    pos, src_idx = orc.positions_dedup(topk, rir, E, R, cap)
+    epr = E // R
+    for fp8 in (False, True):
+        rx, rs, rti, rtw = orc.dispatch_dedup(x, topk, w, pos, E, R, R * cap, fp8)
+        for t in range(T):
+            for j in range(k):
+                p = pos[t, j]
+                if p < 0:
+                    continue
+                d = p // cap
+                assert topk[t, j] // epr == d
+                if fp8:
+                    q, s = orc.quantize_token(x[t])
+                    assert np.array_equal(rx[p], q) and np.array_equal(rs[p], s)
+                else:
+                    assert np.array_equal(rx[p], x[t])
+                for jj in range(k):
+                    e = topk[t, jj]
+                    here = e >= 0 and e // epr == d
+                    assert rti[p, jj] == (e - d * epr if here else -1), (t, j, jj)
+                    assert rtw[p, jj] == (w[t, jj] if here else 0.0)
+
+
+def pin_dedup_prereduce(orc):
+    """Per-expert exchange vs deduplicated exchange with the expert side
+    pre-reducing (weighting and summing the outputs of a row's local experts):
+    on values exact in bf16 and fp32 both give the same combined result."""
+    rng = np.random.default_rng(59)
+    T, k, E, R, H = 48, 4, 16, 4, 128
+    topk = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32)
+    topk[rng.random((T, k)) < 0.1] = -1
+    w = rng.choice(np.array([0.25, 0.5, 1.0, 2.0], np.float32), size=(T, k))
+    L = orc.layout(topk, E, R, 1 << 30)
+    cap = int(L.rank_rows.max())
+    L = orc.layout(topk, E, R, cap)
+    pos, _ = orc.positions(topk, L, E, R, cap)
+    out = bf16_bits_of(rng.integers(-8, 9, size=(R * cap, H)).astype(np.float32))  # per-expert outputs
+    y_ref = orc.combine(out, pos, w)
+    rir, rows, _ = orc.layout_dedup(topk, E, R, cap)
+    pdd, _ = orc.positions_dedup(topk, rir, E, R, cap)
+    _, _, rti, rtw = orc.dispatch_dedup(np.zeros((T, H), np.uint16), topk, w, pdd, E, R, R * cap, False)
+    pre = np.zeros((R * cap, H), np.float32)
+    epr = E // R
+    for t in range(T):
+        for j in range(k):
+            p = pdd[t, j]
+            if p < 0:
+                continue
+            for jj in range(k):
+                if rti[p, jj] >= 0:  # expert rti + d*epr's output row for token t, weighted
+                    assert pos[t, jj] >= 0 and topk[t, jj] == rti[p, jj] + (p // cap) * epr
+                    pre[p] += rtw[p, jj] * f32_of_bf16(out[pos[t, jj]])
+    y_dd = orc.combine(bf16_bits_of(pre), pdd, None)
+    assert np.array_equal(y_dd, y_ref), "dedup + pre-reduction differs from the per-expert combine"
+
+
 ALL_PINS = [
     pin_e4m3_decode, pin_e4m3_encode, pin_bf16_round,
     pin_layout_golden, pin_layout_bruteforce, pin_layout_argsort, pin_layout_invariants,
     pin_dispatch_bf16, pin_fp8_golden, pin_fp8_bound, pin_fp8_torch,
     pin_combine_fp64, pin_combine_order, pin_combine_fma, pin_combine_identity, pin_backward,
+    pin_dedup_golden, pin_dedup_bruteforce, pin_dedup_dispatch, pin_dedup_prereduce,
 ]

@@ -68,6 +68,20 @@ MUTANTS = [
     ("combine drops the last slot",
      "        for (int j = 0; j < k; ++j) {\n            int32_t p = pos[(size_t)t * k + j];\n            if (p < 0) continue;\n            float wt",
      "        for (int j = 0; j < k - 1; ++j) {\n            int32_t p = pos[(size_t)t * k + j];\n            if (p < 0) continue;\n            float wt"),
+    # rank-deduplicated exchange
+    ("dedup leader by expert instead of rank",
+     "if (slot_is_valid(row, jj, E, &ignore) && row[jj] / experts_per_rank == d) leader = 0;",
+     "if (slot_is_valid(row, jj, E, &ignore) && row[jj] == row[j]) leader = 0;"),
+    ("dedup rank is inclusive", "rank_in_rank[(size_t)t * k + j] = fill[d];",
+     "rank_in_rank[(size_t)t * k + j] = fill[d] + 1;"),
+    ("dedup local expert keeps the rank base",
+     "recv_topk_idx[(size_t)p * k + jj] = here ? row[jj] - d * experts_per_rank : -1;",
+     "recv_topk_idx[(size_t)p * k + jj] = here ? row[jj] : -1;"),
+    ("dedup weights of other ranks' slots kept",
+     "recv_topk_w[(size_t)p * k + jj] = here ? topk_w[(size_t)t * k + jj] : 0.0f;",
+     "recv_topk_w[(size_t)p * k + jj] = topk_w[(size_t)t * k + jj];"),
+    ("dedup positions keep the row at cap", "if (r < 0 || (long long)r >= cap_rows) {",
+     "if (r < 0 || (long long)r > cap_rows) {"),
     ("combine_backward copies the wrong token",
      "memcpy(grad_rows + (size_t)p * H, grad_y + (size_t)t * H, sizeof(uint16_t) * (size_t)H);",
      "memcpy(grad_rows + (size_t)p * H, grad_y + (size_t)((t + 1) % T) * H, sizeof(uint16_t) * (size_t)H);"),
