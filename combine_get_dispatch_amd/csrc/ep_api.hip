@@ -151,8 +151,9 @@ int log2_exact(int v) {
     return s;
 }
 
+// mode: 0 = rows from the handle (backward), 1 = per expert, 2 = per rank
 int fill_dispatch(ep_ctx *ctx, const uint16_t *x, const int32_t *topk, const float *w, const ep_layout *L,
-                  bool forward, void *recv_x, float *recv_scales, float *recv_w, ep_handle *h, ep::DispatchArgs &a,
+                  int mode, void *recv_x, float *recv_scales, float *recv_w, ep_handle *h, ep::DispatchArgs &a,
                   Geometry &g) {
     const ep_config &c = ctx->cfg;
     if (!x || (!recv_x && c.cap_rows > 0)) return EP_ERR_ARG;
@@ -167,9 +168,10 @@ int fill_dispatch(ep_ctx *ctx, const uint16_t *x, const int32_t *topk, const flo
     a.recv_w = (w && recv_w) ? recv_w : nullptr;
     a.recv_x = recv_x;
     a.recv_scales = recv_scales;
-    if (forward) {
+    if (mode != 0) {
         a.rank_in_expert = L->rank_in_expert;
         a.expert_off = L->expert_off;
+        a.rank_in_rank = L->rank_in_rank;
     }
     a.T = c.num_tokens;
     a.k = c.num_topk;
@@ -187,17 +189,20 @@ int fill_dispatch(ep_ctx *ctx, const uint16_t *x, const int32_t *topk, const flo
 }
 
 int dispatch_common(ep_ctx *ctx, const uint16_t *x, const int32_t *topk, const float *w, const ep_layout *L,
-                    bool fp8, bool forward, void *recv_x, float *recv_scales, float *recv_w, ep_handle *h,
-                    ep_stream_t stream, const char *name) {
+                    bool fp8, int mode, void *recv_x, float *recv_scales, float *recv_w, ep_handle *h,
+                    ep_stream_t stream, const char *name, int32_t *recv_topk_idx = nullptr,
+                    float *recv_topk_w = nullptr) {
     const ep_config &c = ctx->cfg;
     if (c.num_tokens == 0) return EP_OK;
     ep::DispatchArgs a;
     Geometry g;
-    if (int r = fill_dispatch(ctx, x, topk, w, L, forward, recv_x, recv_scales, recv_w, h, a, g)) return r;
+    if (int r = fill_dispatch(ctx, x, topk, w, L, mode, recv_x, recv_scales, recv_w, h, a, g)) return r;
+    a.recv_topk_idx = recv_topk_idx;
+    a.recv_topk_w = (w && recv_topk_w) ? recv_topk_w : nullptr;
     if (ctx->debug)
         std::fprintf(stderr, "libep: %s T=%d k=%d H=%d fp8=%d waves=%d (%d/token, %d passes each)\n", name,
                      a.T, a.k, a.H, (int)fp8, g.num_waves, g.wpt, g.ppw);
-    return hip_fail(ep::launch_dispatch(a, fp8, forward, g.num_waves, (hipStream_t)stream), name);
+    return hip_fail(ep::launch_dispatch(a, fp8, mode, g.num_waves, (hipStream_t)stream), name);
 }
 
 int fill_layout(ep_ctx *ctx, const int32_t *topk_idx, const ep_layout *L, ep::LayoutArgs &a) {
@@ -238,6 +243,12 @@ int fill_layout(ep_ctx *ctx, const int32_t *topk_idx, const ep_layout *L, ep::La
     a.rank_ready = ctx->rank_ready;
     a.counters = ctx->counters;
     a.spin_limit = ctx->spin_limit;
+    // the deduplicated outputs: both or neither (no tokens: rank_in_rank is empty)
+    if (L->rank_in_rank && !L->token_rows) return EP_ERR_ARG;
+    if (L->token_rows && !L->rank_in_rank && c.num_tokens > 0) return EP_ERR_ARG;
+    if (!aligned(L->rank_in_rank, 16) || !aligned(L->token_rows, 4)) return EP_ERR_ALIGN;
+    a.rank_in_rank = L->rank_in_rank;
+    a.token_rows = L->token_rows;
     return EP_OK;
 }
 
@@ -297,6 +308,10 @@ int ep_query_sizes(const ep_config *cfg, ep_sizes *out) {
     out->recv_scales = rows * (H / 128) * 4;
     out->recv_w = rows * 4;
     out->combined_x = T * H * 2;
+    out->rank_in_rank = T * k * 4;
+    out->token_rows = R * 4;
+    out->recv_topk_idx = rows * k * 4;
+    out->recv_topk_w = rows * k * 4;
     out->workspace = workspace_layout(*cfg).total;
     return EP_OK;
 }
@@ -371,13 +386,28 @@ int ep_dispatch(ep_ctx *ctx, const uint16_t *x, const int32_t *topk_idx, const f
                 ep_handle *handle, ep_stream_t stream) {
     if (int r = check_forward_dispatch(ctx, topk_idx, topk_weights, L, use_fp8, recv_scales, recv_w, handle))
         return r;
-    return dispatch_common(ctx, x, topk_idx, topk_weights, L, use_fp8 != 0, true, recv_x, recv_scales, recv_w,
+    return dispatch_common(ctx, x, topk_idx, topk_weights, L, use_fp8 != 0, 1, recv_x, recv_scales, recv_w,
                            handle, stream, "ep_dispatch");
+}
+
+int ep_dispatch_dedup(ep_ctx *ctx, const uint16_t *x, const int32_t *topk_idx, const float *topk_weights,
+                      const ep_layout *L, int use_fp8, void *recv_x, float *recv_scales, int32_t *recv_topk_idx,
+                      float *recv_topk_w, ep_handle *handle, ep_stream_t stream) {
+    if (int r = check_forward_dispatch(ctx, topk_idx, topk_weights, L, use_fp8, recv_scales, nullptr, handle))
+        return r;
+    const ep_config &c = ctx->cfg;
+    if (c.num_tokens > 0 && !L->rank_in_rank) return EP_ERR_ARG;
+    if (!recv_topk_idx && c.cap_rows > 0) return EP_ERR_ARG;
+    if (recv_topk_w && !topk_weights) return EP_ERR_ARG;
+    if (!aligned(recv_topk_idx, 4) || !aligned(recv_topk_w, 4)) return EP_ERR_ALIGN;
+    return dispatch_common(ctx, x, topk_idx, topk_weights, L, use_fp8 != 0, 2, recv_x, recv_scales, nullptr,
+                           handle, stream, "ep_dispatch_dedup", recv_topk_idx, recv_topk_w);
 }
 
 int ep_dispatch_with_layout(ep_ctx *ctx, const uint16_t *x, const int32_t *topk_idx, const float *topk_weights,
                             const ep_layout *L, int use_fp8, void *recv_x, float *recv_scales, float *recv_w,
                             ep_handle *handle, ep_stream_t stream) {
+    if (L && (L->rank_in_rank || L->token_rows)) return EP_ERR_ARG;  // per-expert rows only
     ep::LayoutArgs la;
     if (int r = fill_layout(ctx, topk_idx, L, la)) return r;
     if (int r = check_forward_dispatch(ctx, topk_idx, topk_weights, L, use_fp8, recv_scales, recv_w, handle))
@@ -387,7 +417,7 @@ int ep_dispatch_with_layout(ep_ctx *ctx, const uint16_t *x, const int32_t *topk_
         return hip_fail(ep::launch_layout(la, (hipStream_t)stream), "ep_dispatch_with_layout");
     ep::DispatchArgs da;
     Geometry g;
-    if (int r = fill_dispatch(ctx, x, topk_idx, topk_weights, L, true, recv_x, recv_scales, recv_w, handle, da, g))
+    if (int r = fill_dispatch(ctx, x, topk_idx, topk_weights, L, 1, recv_x, recv_scales, recv_w, handle, da, g))
         return r;
     if (ctx->debug)
         std::fprintf(stderr, "libep: layout+dispatch T=%d k=%d E=%d R=%d H=%d fp8=%d tiles=%d waves=%d\n", c.num_tokens,
@@ -421,7 +451,7 @@ int ep_combine_backward(ep_ctx *ctx, const uint16_t *grad_combined, const ep_han
     if (!ctx) return EP_ERR_ARG;
     if (int r = check_handle(ctx, handle)) return r;
     ep_handle h = *handle;
-    return dispatch_common(ctx, grad_combined, nullptr, nullptr, nullptr, false, false, grad_rows, nullptr,
+    return dispatch_common(ctx, grad_combined, nullptr, nullptr, nullptr, false, 0, grad_rows, nullptr,
                            nullptr, &h, stream, "ep_combine_backward");
 }
 

@@ -41,6 +41,8 @@ struct LayoutArgs {
     uint32_t *rank_ready;  // [layout blocks] epoch once a block's ranks are written (fused launch)
     uint32_t *counters;
     uint32_t spin_limit;
+    int32_t *rank_in_rank;  // [T][k] or NULL: the deduplicated exchange's rows (leader slots)
+    int32_t *token_rows;    // [R] or NULL
 };
 
 struct DispatchArgs {
@@ -49,6 +51,9 @@ struct DispatchArgs {
     const float *w;              // [T][k] or NULL (forward only)
     const int32_t *rank_in_expert;  // [T][k]     (forward only)
     const int32_t *expert_off;   // [E]           (forward only)
+    const int32_t *rank_in_rank; // [T][k]        (deduplicated forward only)
+    int32_t *recv_topk_idx;      // [R*cap][k]    (deduplicated forward only)
+    float *recv_topk_w;          // [R*cap][k] or NULL (deduplicated forward only)
     int32_t *pos;                // [T][k] written (forward) or read (backward)
     int32_t *src_idx;            // [R*cap] (forward only)
     float *recv_w;               // [R*cap] or NULL (forward only)
@@ -72,7 +77,9 @@ struct CombineArgs {
 };
 
 hipError_t launch_layout(const LayoutArgs &a, hipStream_t s);
-hipError_t launch_dispatch(const DispatchArgs &a, bool fp8, bool forward, int num_waves,
+// mode: 0 = backward (rows from handle positions), 1 = forward per expert,
+// 2 = forward deduplicated per rank
+hipError_t launch_dispatch(const DispatchArgs &a, bool fp8, int mode, int num_waves,
                            hipStream_t s);
 hipError_t launch_dispatch_inblock(const LayoutArgs &la, const DispatchArgs &da, bool fp8, int num_waves,
                                    hipStream_t s);

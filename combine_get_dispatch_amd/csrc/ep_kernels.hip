@@ -422,7 +422,7 @@ __device__ __forceinline__ void layout_block(const LayoutArgs &a, int tile, int 
             for (int d = tid; d < a.R; d += kTileTokens) {
                 const int rows = scan[(d + 1) * a.epr] - scan[d * a.epr];
                 a.rank_rows[d] = rows;
-                if ((int64_t)rows > a.cap_rows) atomicOr(&a.counters[kStatus], kStCap);
+                if (!a.token_rows && (int64_t)rows > a.cap_rows) atomicOr(&a.counters[kStatus], kStCap);
             }
             if (fused) {
                 // expert offsets are readable by the dispatch waves from here on
@@ -512,6 +512,9 @@ __device__ __forceinline__ void layout_block(const LayoutArgs &a, int tile, int 
         __syncthreads();
         for (int key = a.E + tid; key < K; key += kTileTokens)
             tile_counts(masks, wpre, agg, a, K, key, tile, epoch, single);
+    } else if (a.token_rows) {
+        for (int key = a.E + tid; key < K; key += kTileTokens)
+            tile_counts(masks, wpre, agg, a, K, key, tile, epoch, single);
     }
     for (int key = a.E + tid; key < K; key += kTileTokens) lookback_key(tv, key);
     if (publish) __threadfence();  // every wave's prefix stores complete before the flag
@@ -524,6 +527,43 @@ __device__ __forceinline__ void layout_block(const LayoutArgs &a, int tile, int 
             __hip_atomic_store(&a.counters[kTicket], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(&a.counters[kEpoch], ne, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
+    }
+    // the deduplicated rows, when asked for: the leader slot of each of the
+    // token's ranks (its first kept slot there) gets the token's row in that
+    // rank, counted like the per-expert ranks (earlier tiles, earlier waves,
+    // earlier lanes of the rank's token mask); the last tile holds the totals
+    if (a.token_rows) {
+        if (my_token) {
+            const uint64_t below = bit - 1;
+            uint64_t led = 0;
+            int rr[KMAX];
+#pragma unroll
+            for (int j = 0; j < KMAX; ++j) {
+                rr[j] = -1;
+                if (ev[j] < 0) continue;
+                const int d = rank_of(ev[j], a.epr, a.epr_shift);
+                if ((led >> d) & 1) continue;
+                led |= 1ull << d;
+                const int key = a.E + d;
+                rr[j] = excl[key] + wpre[wave * K + key] + __popcll(masks[wave * K + key] & below);
+            }
+            int32_t *out = a.rank_in_rank + (size_t)t * a.k;
+            if ((a.k & 3) == 0) {
+#pragma unroll
+                for (int j = 0; j < KMAX; j += 4)
+                    if (j < a.k) *reinterpret_cast<int4 *>(out + j) = make_int4(rr[j], rr[j + 1], rr[j + 2], rr[j + 3]);
+            } else {
+#pragma unroll
+                for (int j = 0; j < KMAX; ++j)
+                    if (j < a.k) out[j] = rr[j];
+            }
+        }
+        if (last_tile && replica == 0)
+            for (int d = tid; d < a.R; d += kTileTokens) {
+                const int rows = excl[a.E + d] + agg[a.E + d];
+                a.token_rows[d] = rows;
+                if ((int64_t)rows > a.cap_rows) atomicOr(&a.counters[kStatus], kStCap);
+            }
     }
 
     // 7. per-source counts for the source ranks that end in this tile
@@ -635,15 +675,54 @@ __device__ __forceinline__ void wait_for_layout(const LayoutWait &w, int t_first
     __syncthreads();
 }
 
-// Slot j's receive row lives in lane j (lanes >= k hold -1). In a fused
-// launch the layout was written by other blocks of the same grid, so it is
-// read with coherent (agent-scope) loads.
-template <bool FWD, bool FUSED>
+// How a dispatch wave finds its token's receive rows.
+enum SlotMode { kRowsFromHandle = 0, kRowsPerExpert = 1, kRowsPerRank = 2 };
+
+// Slot j's receive row lives in lane j (lanes >= k hold -1). Per expert: from
+// the layout's ranks and expert offsets. Per rank (deduplicated): from the
+// leader slots' ranks, and part 0 of the token also writes each kept row's
+// routing entries. From the handle: the backward pass. In a fused launch the
+// layout was written by other blocks of the same grid, so it is read with
+// coherent (agent-scope) loads.
+template <int MODE, bool FUSED>
 __device__ __forceinline__ int slot_row(const DispatchArgs &a, int t, int lane, int part) {
     int p = -1;
+    if (MODE == kRowsPerRank) {
+        const size_t i = (size_t)t * a.k + lane;
+        int e = -1, kept = 0, d = -1;
+        float wv = 0.0f;
+        if (lane < a.k) {
+            e = a.topk[i];
+            kept = a.rank_in_expert[i] >= 0;
+            if (a.recv_topk_w) wv = a.w[i];
+            const int rr = a.rank_in_rank[i];
+            if (rr >= 0 && e >= 0 && e < a.E) {
+                d = rank_of(e, a.epr, a.epr_shift);
+                if (rr < a.cap_rows) p = (int)((int64_t)d * a.cap_rows + rr);
+            }
+        }
+        if (part == 0) {
+            if (lane < a.k) {
+                a.pos[i] = p;
+                if (p >= 0) a.src_idx[p] = t;
+            }
+            // the routing entries of the row this lane leads: slot jj's
+            // expert index among rank d's experts, and its weight
+            for (int jj = 0; jj < a.k; ++jj) {
+                const int ej = readlane_i(e, jj), kj = readlane_i(kept, jj);
+                const float wj = readlane_f(wv, jj);
+                if (p >= 0) {
+                    const bool here = kj && rank_of(ej, a.epr, a.epr_shift) == d;
+                    a.recv_topk_idx[(size_t)p * a.k + jj] = here ? ej - d * a.epr : -1;
+                    if (a.recv_topk_w) a.recv_topk_w[(size_t)p * a.k + jj] = here ? wj : 0.0f;
+                }
+            }
+        }
+        return p;
+    }
     if (lane < a.k) {
         const size_t i = (size_t)t * a.k + lane;
-        if (FWD) {
+        if (MODE == kRowsPerExpert) {
             const int e = a.topk[i];
             const int r = FUSED ? __hip_atomic_load(a.rank_in_expert + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
                                 : a.rank_in_expert[i];
@@ -785,7 +864,7 @@ __device__ __forceinline__ void store_rows(const DispatchArgs &a, int part, int 
     }
 }
 
-template <bool FP8, bool FWD>
+template <bool FP8, int MODE>
 __global__ __launch_bounds__(kWavesPerBlock * 64) void k_dispatch(DispatchArgs a) {
     const int gw = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
     const int t = gw / a.waves_per_token;
@@ -793,7 +872,7 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void k_dispatch(DispatchArgs a
     if (t >= a.T) return;  // whole wave
     u32x4 v[2 * kMaxPassPerWave];
     load_rows<FP8>(a, t, part, true, v);  // in flight while the slot rows are looked up
-    const int p = slot_row<FWD, false>(a, t, threadIdx.x & 63, part);
+    const int p = slot_row<MODE, false>(a, t, threadIdx.x & 63, part);
     store_rows<FP8>(a, part, p, v);
 }
 
@@ -866,7 +945,7 @@ __device__ __forceinline__ void fused_dispatch_block(const DispatchArgs &da, con
     const int t_last = min((min(gw0 + NW, items) - 1) / da.waves_per_token, da.T - 1);
     wait_for_layout(lw, t_first, max(t_last, t_first));
     if (active) {
-        const int p = slot_row<true, true>(da, t, threadIdx.x & 63, part);
+        const int p = slot_row<kRowsPerExpert, true>(da, t, threadIdx.x & 63, part);
         store_rows<FP8>(da, part, p, v);
     }
 }
@@ -947,7 +1026,7 @@ __global__ __launch_bounds__(kTileTokens) void k_layout_dispatch(LayoutArgs la, 
             u32x4 v[2 * kMaxPassPerWave];
             load_rows<FP8>(da, t, part, true, v);
             wave_wait_for_layout(make_wait(la, epoch, tpb), t);
-            const int p = slot_row<true, true>(da, t, threadIdx.x & 63, part);
+            const int p = slot_row<kRowsPerExpert, true>(da, t, threadIdx.x & 63, part);
             store_rows<FP8>(da, part, p, v);
         }
     } else {
@@ -1151,16 +1230,24 @@ hipError_t launch_dispatch_inblock(const LayoutArgs &la, const DispatchArgs &da,
     return hipGetLastError();
 }
 
-hipError_t launch_dispatch(const DispatchArgs &a, bool fp8, bool forward, int num_waves, hipStream_t s) {
+hipError_t launch_dispatch(const DispatchArgs &a, bool fp8, int mode, int num_waves, hipStream_t s) {
     const dim3 grid((num_waves + kWavesPerBlock - 1) / kWavesPerBlock), block(kWavesPerBlock * 64);
-    if (fp8 && forward)
-        hipLaunchKernelGGL((k_dispatch<true, true>), grid, block, 0, s, a);
-    else if (fp8)
-        hipLaunchKernelGGL((k_dispatch<true, false>), grid, block, 0, s, a);
-    else if (forward)
-        hipLaunchKernelGGL((k_dispatch<false, true>), grid, block, 0, s, a);
-    else
-        hipLaunchKernelGGL((k_dispatch<false, false>), grid, block, 0, s, a);
+    if (mode == kRowsPerExpert) {
+        if (fp8)
+            hipLaunchKernelGGL((k_dispatch<true, kRowsPerExpert>), grid, block, 0, s, a);
+        else
+            hipLaunchKernelGGL((k_dispatch<false, kRowsPerExpert>), grid, block, 0, s, a);
+    } else if (mode == kRowsPerRank) {
+        if (fp8)
+            hipLaunchKernelGGL((k_dispatch<true, kRowsPerRank>), grid, block, 0, s, a);
+        else
+            hipLaunchKernelGGL((k_dispatch<false, kRowsPerRank>), grid, block, 0, s, a);
+    } else {
+        if (fp8)
+            hipLaunchKernelGGL((k_dispatch<true, kRowsFromHandle>), grid, block, 0, s, a);
+        else
+            hipLaunchKernelGGL((k_dispatch<false, kRowsFromHandle>), grid, block, 0, s, a);
+    }
     return hipGetLastError();
 }
 

@@ -39,7 +39,7 @@ class EpConfig(ctypes.Structure):
 
 
 LAYOUT_FIELDS = ("cnt_se", "cnt_sd", "recv_cnt", "expert_off", "rank_rows", "src_expert_off",
-                 "rank_in_expert", "is_token_in_rank")
+                 "rank_in_expert", "is_token_in_rank", "rank_in_rank", "token_rows")
 
 
 class EpLayout(ctypes.Structure):
@@ -53,7 +53,8 @@ class EpHandle(ctypes.Structure):
 
 SIZE_FIELDS = ("cnt_se", "cnt_sd", "recv_cnt", "expert_off", "rank_rows", "src_expert_off",
                "rank_in_expert", "is_token_in_rank", "pos", "src_idx", "x", "recv_x_bf16",
-               "recv_x_fp8", "recv_scales", "recv_w", "combined_x", "workspace")
+               "recv_x_fp8", "recv_scales", "recv_w", "combined_x", "rank_in_rank", "token_rows",
+               "recv_topk_idx", "recv_topk_w", "workspace")
 
 
 class EpSizes(ctypes.Structure):
@@ -74,6 +75,9 @@ SIGNATURES = {
     "ep_dispatch_with_layout": (ctypes.c_int, [c_void_p, c_void_p, c_void_p, c_void_p, ctypes.POINTER(EpLayout),
                                                ctypes.c_int, c_void_p, c_void_p, c_void_p,
                                                ctypes.POINTER(EpHandle), c_void_p]),
+    "ep_dispatch_dedup": (ctypes.c_int, [c_void_p, c_void_p, c_void_p, c_void_p, ctypes.POINTER(EpLayout),
+                                         ctypes.c_int, c_void_p, c_void_p, c_void_p, c_void_p,
+                                         ctypes.POINTER(EpHandle), c_void_p]),
     "ep_combine": (ctypes.c_int, [c_void_p, c_void_p, ctypes.POINTER(EpHandle), c_void_p, c_void_p,
                                   c_void_p]),
     "ep_combine_f32": (ctypes.c_int, [c_void_p, c_void_p, ctypes.POINTER(EpHandle), c_void_p,
@@ -164,6 +168,14 @@ def ep_dispatch_with_layout(ctx: int, x: int, topk_idx: int, topk_weights: Optio
            "ep_dispatch_with_layout")
 
 
+def ep_dispatch_dedup(ctx: int, x: int, topk_idx: int, topk_weights: Optional[int], layout: EpLayout,
+                      use_fp8: int, recv_x: int, recv_scales: Optional[int], recv_topk_idx: Optional[int],
+                      recv_topk_w: Optional[int], handle: EpHandle, stream: int) -> None:
+    _check(load().ep_dispatch_dedup(ctx, x, topk_idx, topk_weights, ctypes.byref(layout), int(use_fp8),
+                                    recv_x, recv_scales, recv_topk_idx, recv_topk_w, ctypes.byref(handle),
+                                    stream), "ep_dispatch_dedup")
+
+
 def ep_combine(ctx: int, expert_out: int, handle: EpHandle, weights: Optional[int],
                combined_x: int, stream: int) -> None:
     _check(load().ep_combine(ctx, expert_out, ctypes.byref(handle), weights, combined_x, stream),
@@ -221,9 +233,11 @@ class Layout:
     src_expert_off: "torch.Tensor"
     rank_in_expert: "torch.Tensor"
     is_token_in_rank: "torch.Tensor"
+    rank_in_rank: Optional["torch.Tensor"] = None   # [T, k] int32, rank-deduplicated exchange only
+    token_rows: Optional["torch.Tensor"] = None     # [R] int32, rank-deduplicated exchange only
 
     def c(self) -> EpLayout:
-        return EpLayout(*[getattr(self, n).data_ptr() for n in LAYOUT_FIELDS])
+        return EpLayout(*[_ptr(getattr(self, n)) for n in LAYOUT_FIELDS])
 
 
 @dataclass
@@ -288,12 +302,15 @@ class Buffer:
     def _empty(self, shape, dtype):
         return self.torch.empty(shape, dtype=dtype, device=self.device)
 
-    def new_layout(self) -> Layout:
+    def new_layout(self, dedup: bool = False) -> Layout:
+        """Layout buffers; ``dedup`` adds the rank-deduplicated outputs."""
         t = self.torch
         T, k, E, R = self.T, self.k, self.E, self.R
         return Layout(self._empty((R, E), t.int32), self._empty((R, R), t.int32), self._empty(E, t.int32),
                       self._empty(E, t.int32), self._empty(R, t.int32), self._empty((R, E), t.int32),
-                      self._empty((T, k), t.int32), self._empty((T, R), t.uint8))
+                      self._empty((T, k), t.int32), self._empty((T, R), t.uint8),
+                      self._empty((T, k), t.int32) if dedup else None,
+                      self._empty(R, t.int32) if dedup else None)
 
     def new_handle(self) -> Handle:
         t = self.torch
@@ -339,6 +356,27 @@ class Buffer:
                                 _stream())
         handle.num_tokens, handle.num_topk = ch.num_tokens, ch.num_topk
         return layout, recv_x, recv_scales, recv_w, handle
+
+    def dispatch_dedup(self, x, topk_idx, topk_weights, layout: Layout, use_fp8: bool, out=None):
+        """Rank-deduplicated dispatch: one row per (token, destination rank).
+        ``layout`` must come from ``get_dispatch_layout`` on a layout made with
+        ``new_layout(dedup=True)``. Returns (recv_x, recv_scales,
+        recv_topk_idx, recv_topk_w, handle)."""
+        t = self.torch
+        if out is None:
+            recv_x = self._empty((self.num_rows, self.H), t.uint8 if use_fp8 else t.bfloat16)
+            recv_scales = self._empty((self.num_rows, self.H // 128), t.float32) if use_fp8 else None
+            recv_topk_idx = self._empty((self.num_rows, self.k), t.int32)
+            recv_topk_w = self._empty((self.num_rows, self.k), t.float32) if topk_weights is not None else None
+            handle = self.new_handle()
+        else:
+            recv_x, recv_scales, recv_topk_idx, recv_topk_w, handle = out
+        ch = handle.c()
+        ep_dispatch_dedup(self.ctx, x.data_ptr(), topk_idx.data_ptr(), _ptr(topk_weights), layout.c(),
+                          int(bool(use_fp8)), recv_x.data_ptr(), _ptr(recv_scales), _ptr(recv_topk_idx),
+                          _ptr(recv_topk_w), ch, _stream())
+        handle.num_tokens, handle.num_topk = ch.num_tokens, ch.num_topk
+        return recv_x, recv_scales, recv_topk_idx, recv_topk_w, handle
 
     def combine(self, expert_out, handle: Handle, weights=None, out=None):
         out = out if out is not None else self._empty((self.T, self.H), self.torch.bfloat16)

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define EP_ABI_VERSION 1
+#define EP_ABI_VERSION 2
 
 /* return codes */
 #define EP_OK 0
@@ -97,6 +97,13 @@ typedef struct {
                                  inside e's rows (absolute row: d*cap_rows + expert_off[e] + this) */
     int32_t *rank_in_expert;  /* [T][k] number of earlier tokens routed to the same expert, -1 if the slot is dropped */
     uint8_t *is_token_in_rank;/* [T][R] 1 if token t has an expert on rank d */
+    /* Rank-deduplicated exchange (optional: both NULL, or both set). The
+     * leader slot of (t, d) is token t's first kept slot whose expert lives
+     * on rank d; rank d's rows hold its tokens in source-token order.
+     * With these set, EP_ST_CAPACITY reports token_rows[d] > cap_rows
+     * (the rows ep_dispatch_dedup writes) instead of rank_rows. */
+    int32_t *rank_in_rank;    /* [T][k] at a leader slot: earlier tokens with a kept slot on the same rank; else -1 */
+    int32_t *token_rows;      /* [R] tokens with a kept slot on rank d (its deduplicated rows) */
 } ep_layout;
 
 /* The routing state dispatch produces and combine / the backward pair reuse
@@ -112,6 +119,7 @@ typedef struct {
     size_t cnt_se, cnt_sd, recv_cnt, expert_off, rank_rows, src_expert_off;
     size_t rank_in_expert, is_token_in_rank, pos, src_idx;
     size_t x, recv_x_bf16, recv_x_fp8, recv_scales, recv_w, combined_x;
+    size_t rank_in_rank, token_rows, recv_topk_idx, recv_topk_w; /* rank-deduplicated exchange */
     size_t workspace; /* device bytes ep_create allocates */
 } ep_sizes;
 
@@ -143,8 +151,10 @@ int ep_destroy(ep_ctx *ctx);
  * EP_ST_BAD_EXPERT and is dropped; a repeat of an expert already in the
  * token sets EP_ST_DUP_EXPERT and is dropped. rank_rows[d] > cap_rows sets
  * EP_ST_CAPACITY. One kernel launch; uses the ctx workspace.
- * topk_idx: [T][k] int32. All layout pointers must be non-NULL (T = 0 allowed);
- * rank_in_expert and is_token_in_rank 16-byte aligned, the others 4-byte. */
+ * topk_idx: [T][k] int32. All layout pointers must be non-NULL (T = 0 allowed)
+ * except rank_in_rank and token_rows, which are computed only when both are
+ * set (the rank-deduplicated exchange); rank_in_expert, is_token_in_rank and
+ * rank_in_rank 16-byte aligned, the others 4-byte. */
 int ep_get_dispatch_layout(ep_ctx *ctx, const int32_t *topk_idx, const ep_layout *layout,
                            ep_stream_t stream);
 
@@ -174,12 +184,33 @@ int ep_dispatch(ep_ctx *ctx, const uint16_t *x, const int32_t *topk_idx,
  * LDS (no block waits on another); beyond that the layout blocks raise flags
  * in the workspace and the dispatch waves, which have already loaded their
  * rows of x, wait on them only to place the rows. Same arguments and
- * requirements as the two calls it replaces; calls on one context are
- * ordered by the stream (two streams sharing a context race). */
+ * requirements as the two calls it replaces (a layout with rank_in_rank or
+ * token_rows set: EP_ERR_ARG); calls on one context are ordered by the
+ * stream (two streams sharing a context race). */
 int ep_dispatch_with_layout(ep_ctx *ctx, const uint16_t *x, const int32_t *topk_idx,
                             const float *topk_weights, const ep_layout *layout, int use_fp8,
                             void *recv_x, float *recv_scales, float *recv_w, ep_handle *handle,
                             ep_stream_t stream);
+
+/* Rank-deduplicated dispatch (the pages' normal kernels send a token once
+ * per destination rank): for every leader slot (t, j) of rank d (see
+ * ep_layout), writes handle->pos[t][j] = d*cap_rows + rank_in_rank[t][j]
+ * (-1 if that reaches cap_rows; -1 for every slot that is not a leader),
+ * src_idx[pos] = t, token t's row once (bf16 copy, or e4m3 + scales as in
+ * ep_dispatch), and the row's routing entries: for every slot j' of t,
+ *   recv_topk_idx[pos][j'] = e' - d*E/R and recv_topk_w[pos][j'] = topk_weights[t][j']
+ * if slot j' is kept and its expert e' lives on rank d, else -1 and 0.
+ * The layout must come from ep_get_dispatch_layout with rank_in_rank and
+ * token_rows set. recv_topk_idx: [R*cap_rows][k] int32 (required);
+ * recv_topk_w: [R*cap_rows][k] fp32 (NULL: not written; requires
+ * topk_weights). The expert side then reduces each row over its local
+ * experts with these weights; ep_combine with weights NULL on this handle
+ * sums a token's pre-reduced rows (one per destination rank) in slot order.
+ * Same stream, alignment and error rules as ep_dispatch. */
+int ep_dispatch_dedup(ep_ctx *ctx, const uint16_t *x, const int32_t *topk_idx,
+                      const float *topk_weights, const ep_layout *layout, int use_fp8,
+                      void *recv_x, float *recv_scales, int32_t *recv_topk_idx, float *recv_topk_w,
+                      ep_handle *handle, ep_stream_t stream);
 
 /* Combine (the guide's combine): weighted gather-reduce back to source-token
  * order. For each token t and channel i: acc = +0.0f; for j = 0..k-1 with

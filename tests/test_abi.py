@@ -47,7 +47,7 @@ def test_extern_c_symbols_unmangled(lib):
 
 
 def test_version_and_strerror(lib):
-    assert ep.ep_version() == 1
+    assert ep.ep_version() == 2
     assert ep.ep_strerror(0) == "ok"
     assert "argument" in ep.ep_strerror(-1)
     assert "align" in ep.ep_strerror(-2)
@@ -78,6 +78,8 @@ def test_query_sizes_values(lib):
     assert s.pos == s.rank_in_expert == 4096 * 8 * 4
     assert s.is_token_in_rank == 4096 * 32
     assert s.cnt_se == s.src_expert_off == 32 * 256 * 4 and s.cnt_sd == 32 * 32 * 4
+    assert s.rank_in_rank == 4096 * 8 * 4 and s.token_rows == 32 * 4
+    assert s.recv_topk_idx == s.recv_topk_w == rows * 8 * 4
     assert s.workspace >= 16 * 4 + 33 * 288 * 4  # counters + boundary prefixes (+ tile states)
     ep.ep_query_sizes(cfg(T=0))  # empty input is a valid config
 
@@ -89,6 +91,7 @@ def test_null_args_rejected_without_gpu(lib):
     assert L.ep_create(ctypes.byref(cfg(T=63)), ctypes.byref(out)) == ep.EP_ERR_ARG and not out.value
     assert L.ep_get_dispatch_layout(None, None, None, None) == ep.EP_ERR_ARG
     assert L.ep_combine(None, None, None, None, None, None) == ep.EP_ERR_ARG
+    assert L.ep_dispatch_dedup(None, None, None, None, None, 0, None, None, None, None, None, None) == ep.EP_ERR_ARG
     assert L.ep_destroy(None) == ep.EP_OK
     assert L.ep_copy_bytes(None, None, 0, None) == ep.EP_OK
     assert L.ep_copy_bytes(None, None, 16, None) == ep.EP_ERR_ARG
