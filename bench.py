@@ -116,6 +116,59 @@ class Path:
         return int((self.handle.pos >= 0).sum().item())
 
 
+def dedup_bytes(T, k, H, Nd, use_fp8):
+    """Algorithmic bytes of the rank-deduplicated step (Nd = rows, one per
+    (token, destination rank)): dispatch reads x and the weights, writes the
+    rows (+ scales) and each row's k routing entries (index + weight); the
+    combine of the pre-reduced rows reads them and writes y."""
+    G = H // 128
+    row = H + 4 * G if use_fp8 else 2 * H
+    d = 2 * T * H + Nd * row + 8 * Nd * k + 4 * T * k
+    c = 2 * Nd * H + 2 * T * H + 4 * T * k
+    return d, c
+
+
+class DedupPath:
+    """The rank-deduplicated form of a workload's step: layout with the
+    leader ranks, one row per (token, destination rank), combine of the
+    pre-reduced rows (unit weights)."""
+
+    def __init__(self, main, torch, ep, workloads, seed):
+        cfg = main.cfg
+        self.main = main
+        probe = ep.Buffer(cfg.T, cfg.H, cfg.k, cfg.E, cfg.R, cfg.T)
+        Lp = probe.get_dispatch_layout(main.topk, probe.new_layout(dedup=True))
+        self.cap = int(Lp.token_rows.max().item()) if cfg.T else 0
+        probe.status()
+        probe.close()
+        self.buf = ep.Buffer(cfg.T, cfg.H, cfg.k, cfg.E, cfg.R, self.cap)
+        b = self.buf
+        n = b.num_rows
+        self.layout = b.new_layout(dedup=True)
+        self.recv_x = torch.empty((n, cfg.H), dtype=torch.uint8 if cfg.use_fp8 else torch.bfloat16, device="cuda")
+        self.recv_scales = torch.empty((n, cfg.H // 128), dtype=torch.float32, device="cuda") if cfg.use_fp8 else None
+        self.recv_topk_idx = torch.empty((n, cfg.k), dtype=torch.int32, device="cuda")
+        self.recv_topk_w = torch.empty((n, cfg.k), dtype=torch.float32, device="cuda")
+        self.handle = b.new_handle()
+        self.expert_out = workloads.device_normal_bf16((n, cfg.H), seed=seed + 303)
+        self.y = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device="cuda")
+
+    def layout_op(self):
+        self.buf.get_dispatch_layout(self.main.topk, self.layout)
+
+    def dispatch_op(self):
+        m = self.main
+        self.buf.dispatch_dedup(m.x, m.topk, m.w, self.layout, m.cfg.use_fp8,
+                                out=(self.recv_x, self.recv_scales, self.recv_topk_idx, self.recv_topk_w,
+                                     self.handle))
+
+    def combine_op(self):
+        self.buf.combine(self.expert_out, self.handle, None, out=self.y)
+
+    def rows(self):
+        return int((self.handle.pos >= 0).sum().item())
+
+
 def timed(torch, ops, K, W):
     """W untimed warmups, then exactly K steps between synchronizations; HIP
     events (torch's current stream = the launch stream) bracket every op."""
@@ -483,6 +536,32 @@ def main():
         out["copy_reference"] = {"bytes_moved": 2 * nb, "us": round(copy_ms * 1e3, 2),
                                  "GBps": round(2 * nb / (copy_ms * 1e-3) / 1e9, 1)}
         del src, dst
+    if not args.no_extras:
+        # rank-deduplicated exchange on the same inputs: one row per
+        # (token, destination rank), combine of the pre-reduced rows
+        dp = DedupPath(main_path, torch, ep, workloads, args.seed)
+        ops = [dp.layout_op, dp.dispatch_op, dp.combine_op]
+        e_ms, (l_, d_, c_) = timed(torch, ops, K, W)
+        g_ms, _, _ = graph_step_timed(torch, ops, K, W)
+        if dp.buf.status():
+            raise SystemExit(f"bench: device status {dp.buf.status()} on {cfg.name} (dedup)")
+        Nd = dp.rows()
+        dd, dc = dedup_bytes(cfg.T, cfg.k, cfg.H, Nd, cfg.use_fp8)
+        out["dedup"] = {"workload": cfg.name, "rows": Nd, "rows_per_expert_path": N, "cap_rows": dp.cap,
+                        "us_per_step_graph": round(g_ms * 1e3, 2), "us_per_step_eager": round(e_ms * 1e3, 2),
+                        "layout_us": round(l_ * 1e3, 2),
+                        "dispatch": {"us": round(d_ * 1e3, 2), "bytes": dd,
+                                     "GBps": round(dd / (d_ * 1e-3) / 1e9, 1),
+                                     "frac": round(dd / (d_ * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+                        "combine": {"us": round(c_ * 1e3, 2), "bytes": dc,
+                                    "GBps": round(dc / (c_ * 1e-3) / 1e9, 1),
+                                    "frac": round(dc / (c_ * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+                        "GBps_graph": round((dd + dc) / (g_ms * 1e-3) / 1e9, 1),
+                        "speedup_vs_per_expert_step": round(ms / g_ms, 3)}
+        print(f"# dedup: {g_ms * 1e3:.1f} us/step graph, rows {Nd} of {N}", file=sys.stderr, flush=True)
+        dp.buf.close()
+        del dp
+
     if not args.no_extras and not args.no_decode:
         # decode latency: 128 tokens (one rank's share) and the 8-rank group.
         # The step is launch-bound, so it is captured in a HIP graph and
