@@ -169,6 +169,104 @@ class DedupPath:
         return int((self.handle.pos >= 0).sum().item())
 
 
+def stream_timed(torch, stream, ops, K, W):
+    """ops launched K times back to back on one stream (after W), timed by
+    events on that stream: no cross-queue waits inside the timed region."""
+    with torch.cuda.stream(stream):
+        for _ in range(W):
+            for op in ops:
+                op()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(K):
+            for op in ops:
+                op()
+        e1.record(stream)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / K
+
+
+def concurrent_timed(torch, streams_ops, K, W):
+    """Each (stream, ops) pair launched on its own stream at once, the host
+    synchronizing between repetitions; a repetition lasts from the earliest
+    start event to the latest end event (one device clock for all streams).
+    Returns the mean over K repetitions (after W)."""
+    reps = []
+    for i in range(W + K):
+        torch.cuda.synchronize()
+        marks = []
+        for st, ops in streams_ops:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            with torch.cuda.stream(st):
+                for op in ops:
+                    op()
+            e1.record(st)
+            marks.append((e0, e1))
+        if i >= W:
+            reps.append(marks)
+    torch.cuda.synchronize()
+    total = 0.0
+    for marks in reps:
+        ref = marks[0][0]
+        starts = [ref.elapsed_time(a) for a, _ in marks]
+        ends = [ref.elapsed_time(b) for _, b in marks]
+        total += max(ends) - min(starts)
+    return total / K
+
+
+def units_used(torch, ep, stream):
+    """Distinct compute units a census launch on `stream` ran on."""
+    with torch.cuda.stream(stream):
+        ids = ep.cu_census(8192)
+    stream.synchronize()
+    return int(torch.unique(ids).numel())
+
+
+def cu_cap_overlap(torch, ep, p, K, W):
+    """The exchange step (fused layout+dispatch, combine) on a stream held to
+    n compute units while a bf16 GEMM runs on the other units: time of each
+    alone and of both at once."""
+    M, Kd, Nn = 4096, 7168, 4096
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    a = torch.randn((M, Kd), generator=g, device="cuda").to(torch.bfloat16)
+    b = torch.randn((Kd, Nn), generator=g, device="cuda").to(torch.bfloat16).contiguous()
+    c = torch.empty((M, Nn), dtype=torch.bfloat16, device="cuda")
+
+    def gemm():
+        torch.matmul(a, b, out=c)
+
+    ep_ops = [p.fused_op, p.combine_op]
+    full, other = torch.cuda.Stream(), torch.cuda.Stream()
+    gemm_full = stream_timed(torch, full, [gemm], K, W)
+    ep_full = stream_timed(torch, full, ep_ops, K, W)
+    both_full = concurrent_timed(torch, [(full, ep_ops), (other, [gemm])], K, W)
+    flops = 2.0 * M * Kd * Nn
+    res = {"gemm": {"shape_mkn": [M, Kd, Nn], "dtype": "bf16", "us": round(gemm_full * 1e3, 2),
+                    "TFLOPs": round(flops / (gemm_full * 1e-3) / 1e12, 1)},
+           "exchange_us": round(ep_full * 1e3, 2),
+           "serial_us": round((gemm_full + ep_full) * 1e3, 2),
+           "by_cus": {"256 (shared, no cap)": {"both_us": round(both_full * 1e3, 2)}}}
+    for n in (32, 64, 128, 192):
+        p.buf.set_num_cus(n)
+        with ep.CuStream(n) as cs, ep.CuStream(n, exclude=True) as rest:
+            units = [units_used(torch, ep, st) for st in (cs.torch_stream, rest.torch_stream)]
+            e_ms = stream_timed(torch, cs.torch_stream, ep_ops, K, W)
+            g_ms = stream_timed(torch, rest.torch_stream, [gemm], K, W)
+            b_ms = concurrent_timed(torch, [(cs.torch_stream, ep_ops), (rest.torch_stream, [gemm])], K, W)
+        p.buf.set_num_cus(0)
+        res["by_cus"][str(n)] = {"units_seen": units, "exchange_alone_us": round(e_ms * 1e3, 2),
+                                 "gemm_on_other_units_us": round(g_ms * 1e3, 2),
+                                 "both_us": round(b_ms * 1e3, 2)}
+    if p.buf.status():
+        raise SystemExit(f"bench: device status {p.buf.status()} in the overlap runs")
+    del a, b, c
+    return res
+
+
 def timed(torch, ops, K, W):
     """W untimed warmups, then exactly K steps between synchronizations; HIP
     events (torch's current stream = the launch stream) bracket every op."""
@@ -561,6 +659,10 @@ def main():
         print(f"# dedup: {g_ms * 1e3:.1f} us/step graph, rows {Nd} of {N}", file=sys.stderr, flush=True)
         dp.buf.close()
         del dp
+
+    if not args.no_extras:
+        out["cu_cap_overlap"] = cu_cap_overlap(torch, ep, main_path, K, W)
+        print("# overlap: " + json.dumps(out["cu_cap_overlap"]), file=sys.stderr, flush=True)
 
     if not args.no_extras and not args.no_decode:
         # decode latency: 128 tokens (one rank's share) and the 8-rank group.

@@ -1,6 +1,7 @@
 // ep_api.hip -- host side of the C ABI declared in include/ep.h: argument
 // validation, the per-context workspace, launch geometry and status words.
 // Every step of the hot path runs in the kernels of ep_kernels.hip.
+#include <algorithm>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -24,7 +25,8 @@ struct ep_ctx {
     uint32_t spin_limit;
     bool debug;
     int cu_count;
-    int fused_resident[2][2];  // [k > 8][fp8]: fused-kernel blocks the GPU holds at once (-1: not asked yet)
+    int fused_per_cu[2][2];    // [k > 8][fp8]: fused-kernel blocks one CU holds at once (-1: not asked yet)
+    int cu_budget;             // compute units the caller's stream may use (ep_set_cu_budget; 0 = all)
 };
 
 namespace {
@@ -336,7 +338,8 @@ int ep_create(const ep_config *cfg, ep_ctx **out) {
         delete ctx;
         return EP_ERR_HIP;
     }
-    for (auto &row : ctx->fused_resident) row[0] = row[1] = -1;
+    for (auto &row : ctx->fused_per_cu) row[0] = row[1] = -1;
+    ctx->cu_budget = 0;
     if (hipMalloc(&ctx->ws, ctx->ws_bytes) != hipSuccess) {
         delete ctx;
         return EP_ERR_NOMEM;
@@ -428,11 +431,11 @@ int ep_dispatch_with_layout(ep_ctx *ctx, const uint16_t *x, const int32_t *topk_
     if (ctx->num_tiles == 1 && ep::inblock_lds_bytes(keys, c.num_topk) <= ep::kMaxBlockLds)
         return hip_fail(ep::launch_dispatch_inblock(la, da, use_fp8 != 0, g.num_waves, (hipStream_t)stream),
                         "ep_dispatch_with_layout");
-    int &resident = ctx->fused_resident[c.num_topk > 8][use_fp8 != 0];
-    if (resident < 0)
-        resident = ctx->cu_count * ep::layout_dispatch_blocks_per_cu(c.num_topk, use_fp8 != 0,
-                                                                     ep::layout_lds_bytes(keys));
-    return hip_fail(ep::launch_layout_dispatch(la, da, use_fp8 != 0, g.num_waves, resident, (hipStream_t)stream),
+    int &per_cu = ctx->fused_per_cu[c.num_topk > 8][use_fp8 != 0];
+    if (per_cu < 0)
+        per_cu = ep::layout_dispatch_blocks_per_cu(c.num_topk, use_fp8 != 0, ep::layout_lds_bytes(keys));
+    const int cus = ctx->cu_budget > 0 ? std::min(ctx->cu_budget, ctx->cu_count) : ctx->cu_count;
+    return hip_fail(ep::launch_layout_dispatch(la, da, use_fp8 != 0, g.num_waves, cus * per_cu, (hipStream_t)stream),
                     "ep_dispatch_with_layout");
 }
 
@@ -469,6 +472,64 @@ int ep_get_status(ep_ctx *ctx, ep_stream_t stream, uint32_t *status) {
     if (r) return r;
     const uint32_t zero = 0;
     return hip_fail(hipMemcpy(ctx->counters + ep::kStatus, &zero, sizeof zero, hipMemcpyHostToDevice), "hipMemcpy");
+}
+
+int ep_set_cu_budget(ep_ctx *ctx, int num_cus) {
+    if (!ctx || num_cus < 0) return EP_ERR_ARG;
+    ctx->cu_budget = num_cus;
+    return EP_OK;
+}
+
+int ep_cu_mask(int cu_count, int num_cus, int exclude, uint32_t *mask, int words) {
+    constexpr int kXcds = 8;
+    if (!mask || cu_count <= 0 || cu_count % (8 * kXcds) || words < cu_count / 32) return EP_ERR_ARG;
+    if (num_cus <= 0 || num_cus > cu_count || num_cus % kXcds || (exclude && num_cus == cu_count))
+        return EP_ERR_ARG;
+    // per XCD a, m units at offsets a*m .. a*m+m-1 (mod per): m per XCD when
+    // bit i belongs to XCD i / per, and, since the 8m offsets run through
+    // consecutive values and per is a multiple of 8, m per XCD when bit i
+    // belongs to XCD i mod 8 as well
+    const int per = cu_count / kXcds, m = num_cus / kXcds;
+    for (int w = 0; w < words; ++w) mask[w] = 0;
+    for (int a = 0; a < kXcds; ++a)
+        for (int j = 0; j < m; ++j) {
+            const int bit = a * per + (a * m + j) % per;
+            mask[bit / 32] |= 1u << (bit % 32);
+        }
+    if (exclude)
+        for (int w = 0; w < cu_count / 32; ++w) mask[w] = ~mask[w];
+    return EP_OK;
+}
+
+int ep_stream_create_cus(int num_cus, int exclude, ep_stream_t *out) {
+    if (!out) return EP_ERR_ARG;
+    *out = nullptr;
+    int dev = 0, cus = 0;
+    if (int r = hip_fail(hipGetDevice(&dev), "hipGetDevice")) return r;
+    if (int r = hip_fail(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev),
+                         "hipDeviceGetAttribute"))
+        return r;
+    uint32_t mask[64];
+    if (cus > 64 * 32) return EP_ERR_ARG;
+    if (int r = ep_cu_mask(cus, num_cus, exclude, mask, cus / 32)) return r;
+    hipStream_t s = nullptr;
+    const hipError_t e = (!exclude && num_cus == cus) ? hipStreamCreate(&s)
+                                                      : hipExtStreamCreateWithCUMask(&s, cus / 32, mask);
+    if (int r = hip_fail(e, "hipExtStreamCreateWithCUMask")) return r;
+    *out = s;
+    return EP_OK;
+}
+
+int ep_stream_destroy(ep_stream_t stream) {
+    if (!stream) return EP_OK;
+    return hip_fail(hipStreamDestroy((hipStream_t)stream), "hipStreamDestroy");
+}
+
+int ep_cu_census(int blocks, int naps, uint32_t *ids, ep_stream_t stream) {
+    if (blocks == 0) return EP_OK;
+    if (blocks < 0 || blocks > (1 << 20) || naps < 0 || naps > 64 || !ids) return EP_ERR_ARG;
+    if (!aligned(ids, 4)) return EP_ERR_ALIGN;
+    return hip_fail(ep::launch_cu_census(blocks, naps, ids, (hipStream_t)stream), "ep_cu_census");
 }
 
 int ep_copy_bytes(const void *src, void *dst, size_t bytes, ep_stream_t stream) {

@@ -89,5 +89,6 @@ hipError_t launch_layout_dispatch(const LayoutArgs &la, const DispatchArgs &da, 
 int layout_dispatch_blocks_per_cu(int k, bool fp8, size_t lds);
 hipError_t launch_combine(const CombineArgs &a, bool out_f32, int num_waves, hipStream_t s);
 hipError_t launch_copy(const void *src, void *dst, size_t n16, hipStream_t s);
+hipError_t launch_cu_census(int blocks, int naps, uint32_t *ids, hipStream_t s);
 
 }  // namespace ep

@@ -16,6 +16,7 @@
 //               (all slots in flight) and accumulates in fp32 with one fused
 //               multiply-add per slot in slot order, then rounds to bf16.
 //   k_copy      plain 128-bit streaming copy (bandwidth calibration).
+//   k_cu_census the compute unit each workgroup runs on (checks stream CU masks).
 //
 // The operations follow the DeepEP usage guide's dispatch / combine /
 // backward interface (zhouruolin.cn DeepEP guide, section 5); the arithmetic
@@ -1161,6 +1162,18 @@ __global__ __launch_bounds__(256) void k_copy(const u32x4 *__restrict__ src, u32
         __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
 }
 
+// Workgroup b records the unit it runs on: XCC_ID (hardware register 20) and
+// the shader engine / array / CU fields of HW_ID (register 4, bits 8..15),
+// then sleeps so the launch cannot finish on a few units.
+__global__ __launch_bounds__(64) void k_cu_census(uint32_t *__restrict__ ids, int naps) {
+    if (threadIdx.x == 0) {
+        const uint32_t hw = __builtin_amdgcn_s_getreg((31 << 11) | 4);
+        const uint32_t xcc = __builtin_amdgcn_s_getreg((3 << 11) | 20) & 15u;
+        ids[blockIdx.x] = (xcc << 16) | ((hw >> 8) & 0xFFu);
+    }
+    for (int i = 0; i < naps; ++i) __builtin_amdgcn_s_sleep(127);
+}
+
 }  // namespace
 
 hipError_t launch_layout(const LayoutArgs &a, hipStream_t s) {
@@ -1257,6 +1270,11 @@ hipError_t launch_combine(const CombineArgs &a, bool out_f32, int num_waves, hip
         hipLaunchKernelGGL(k_combine<true>, grid, block, 0, s, a);
     else
         hipLaunchKernelGGL(k_combine<false>, grid, block, 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_cu_census(int blocks, int naps, uint32_t *ids, hipStream_t s) {
+    hipLaunchKernelGGL(k_cu_census, dim3(blocks), dim3(64), 0, s, ids, naps);
     return hipGetLastError();
 }
 

@@ -88,6 +88,12 @@ SIGNATURES = {
                                             c_void_p, c_void_p]),
     "ep_get_status": (ctypes.c_int, [c_void_p, c_void_p, ctypes.POINTER(ctypes.c_uint32)]),
     "ep_copy_bytes": (ctypes.c_int, [c_void_p, c_void_p, ctypes.c_size_t, c_void_p]),
+    "ep_cu_mask": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_uint32),
+                                  ctypes.c_int]),
+    "ep_stream_create_cus": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.POINTER(c_void_p)]),
+    "ep_stream_destroy": (ctypes.c_int, [c_void_p]),
+    "ep_set_cu_budget": (ctypes.c_int, [c_void_p, ctypes.c_int]),
+    "ep_cu_census": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, c_void_p, c_void_p]),
 }
 
 _lib = None
@@ -213,6 +219,32 @@ def ep_copy_bytes(src: int, dst: int, nbytes: int, stream: int) -> None:
 # ---------------------------------------------------------------------------
 # torch convenience layer (allocation + pointer marshalling only)
 # ---------------------------------------------------------------------------
+
+def ep_cu_mask(cu_count: int, num_cus: int, exclude: bool = False) -> list:
+    """The compute-unit mask as a list of 32-bit words (host only)."""
+    words = max(cu_count // 32, 1)
+    buf = (ctypes.c_uint32 * words)()
+    _check(load().ep_cu_mask(cu_count, num_cus, int(bool(exclude)), buf, words), "ep_cu_mask")
+    return list(buf)
+
+
+def ep_stream_create_cus(num_cus: int, exclude: bool = False) -> int:
+    out = c_void_p()
+    _check(load().ep_stream_create_cus(num_cus, int(bool(exclude)), ctypes.byref(out)), "ep_stream_create_cus")
+    return out.value
+
+
+def ep_set_cu_budget(ctx: int, num_cus: int) -> None:
+    _check(load().ep_set_cu_budget(ctx, num_cus), "ep_set_cu_budget")
+
+
+def ep_stream_destroy(stream: int) -> None:
+    _check(load().ep_stream_destroy(stream), "ep_stream_destroy")
+
+
+def ep_cu_census(blocks: int, naps: int, ids: int, stream: int) -> None:
+    _check(load().ep_cu_census(blocks, naps, ids, stream), "ep_cu_census")
+
 
 def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
@@ -399,9 +431,48 @@ class Buffer:
                              _stream())
         return out
 
+    def set_num_cus(self, num_cus: int) -> None:
+        """The compute units the stream these calls run on may use (0 = all);
+        see CuStream."""
+        ep_set_cu_budget(self.ctx, num_cus)
+
     def status(self) -> int:
         """Synchronize the current stream; return and clear the sticky status bits."""
         return ep_get_status(self.ctx, _stream())
+
+
+class CuStream:
+    """A HIP stream whose kernels run on `num_cus` compute units (or on the
+    others, exclude=True), wrapped as a torch external stream; use it with
+    ``torch.cuda.stream(s.torch_stream)`` so the ep calls and torch work
+    issued inside launch on it. close() destroys the HIP stream."""
+
+    def __init__(self, num_cus: int, exclude: bool = False):
+        import torch
+        self.num_cus, self.exclude = num_cus, exclude
+        self.handle = ep_stream_create_cus(num_cus, exclude)
+        self.torch_stream = torch.cuda.ExternalStream(self.handle)
+
+    def close(self):
+        if self.handle:
+            self.torch_stream.synchronize()
+            ep_stream_destroy(self.handle)
+            self.handle = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+
+def cu_census(blocks: int = 8192, naps: int = 2):
+    """The compute units a launch of `blocks` workgroups on the current stream
+    ran on (a uint32 tensor of (XCD << 16) | unit bits, one per workgroup)."""
+    import torch
+    ids = torch.empty(blocks, dtype=torch.int32, device="cuda")
+    ep_cu_census(blocks, naps, ids.data_ptr(), _stream())
+    return ids
 
 
 def copy_bytes(src, dst) -> None:

@@ -243,6 +243,45 @@ int ep_dispatch_backward(ep_ctx *ctx, const uint16_t *grad_rows, const ep_handle
  * them. Returns EP_OK or EP_ERR_HIP. */
 int ep_get_status(ep_ctx *ctx, ep_stream_t stream, uint32_t *status);
 
+/* Compute-unit cap ([Notes] §2: the normal kernels can be held to a chosen
+ * number of SMs so that the rest stay free for computation running beside
+ * them). On this GPU the cap is a property of the stream: kernels launched on
+ * the stream ep_stream_create_cus returns run only on the compute units its
+ * mask enables, and the GEMM or other work that should overlap the exchange
+ * runs on another stream (for instance the complementary one, exclude = 1).
+ *
+ * ep_cu_mask (host only, no GPU needed) fills mask[0..words) (bit i = compute
+ * unit i of cu_count, 32 per word) with num_cus enabled units, num_cus/8 on
+ * each of the 8 XCDs whether the hardware assigns mask bit i to XCD i mod 8
+ * or to XCD i / (cu_count/8): XCD a enables units a*per + ((a*m + j) mod per),
+ * j < m, with per = cu_count/8 and m = num_cus/8. exclude = 1 inverts the
+ * mask (the other cu_count - num_cus units). Requires cu_count % 64 == 0,
+ * 0 < num_cus <= cu_count, num_cus % 8 == 0, words >= cu_count/32, and not
+ * (exclude and num_cus == cu_count); else EP_ERR_ARG.
+ *
+ * ep_stream_create_cus creates a default-priority HIP stream on the current
+ * device with that mask (exclude = 0 and num_cus = all units: a plain
+ * stream); the caller owns it and releases it with ep_stream_destroy. Any
+ * ep_* call takes it as its stream; results are bit-identical on every
+ * stream. */
+int ep_cu_mask(int cu_count, int num_cus, int exclude, uint32_t *mask, int words);
+/* The streams are blocking streams (they order with the null stream as
+ * hipStreamCreate's do). ep_set_cu_budget tells a context how many compute
+ * units the stream its calls run on may use (0 = all): the fused call sizes
+ * the work its layout blocks take over from it, so that a capped stream does
+ * not leave dispatch blocks queued behind blocks that wait. Results do not
+ * depend on it. */
+int ep_set_cu_budget(ep_ctx *ctx, int num_cus);
+int ep_stream_create_cus(int num_cus, int exclude, ep_stream_t *out);
+int ep_stream_destroy(ep_stream_t stream);
+
+/* Measurement utility: launch `blocks` one-wave workgroups on `stream`; entry
+ * b of ids (device, [blocks] uint32) receives the compute unit workgroup b
+ * ran on, as (XCD id << 16) | (shader engine, array and unit bits of the
+ * wave's hardware id); each workgroup then sleeps about `naps` x 3.4 us so
+ * that the launch spreads over every unit the stream may use. */
+int ep_cu_census(int blocks, int naps, uint32_t *ids, ep_stream_t stream);
+
 /* Measurement utility: copy `bytes` (a multiple of 16, both pointers 16-byte
  * aligned) with a plain streaming-copy kernel, used to calibrate memory
  * counters and as the attainable-bandwidth reference. */

@@ -95,3 +95,42 @@ def test_null_args_rejected_without_gpu(lib):
     assert L.ep_destroy(None) == ep.EP_OK
     assert L.ep_copy_bytes(None, None, 0, None) == ep.EP_OK
     assert L.ep_copy_bytes(None, None, 16, None) == ep.EP_ERR_ARG
+
+
+def _xcd_counts(mask, cu_count, interleaved):
+    per = cu_count // 8
+    counts = [0] * 8
+    for i in range(cu_count):
+        if (mask[i // 32] >> (i % 32)) & 1:
+            counts[i % 8 if interleaved else i // per] += 1
+    return counts
+
+
+@pytest.mark.parametrize("num_cus", [8, 32, 64, 128, 200, 248, 256])
+def test_cu_mask_same_count_on_every_xcd(lib, num_cus):
+    """num_cus/8 units on each XCD under either assignment of mask bits to
+    XCDs (bit i on XCD i mod 8, or on XCD i / 32); the complement holds the
+    rest, again evenly."""
+    C = 256
+    m = ep.ep_cu_mask(C, num_cus)
+    assert sum(bin(w).count("1") for w in m) == num_cus
+    for inter in (False, True):
+        assert _xcd_counts(m, C, inter) == [num_cus // 8] * 8
+    if num_cus < C:
+        c = ep.ep_cu_mask(C, num_cus, exclude=True)
+        assert all((a & b) == 0 for a, b in zip(m, c)) and all((a | b) == 0xFFFFFFFF for a, b in zip(m, c))
+        for inter in (False, True):
+            assert _xcd_counts(c, C, inter) == [(C - num_cus) // 8] * 8
+
+
+@pytest.mark.parametrize("bad", [dict(num_cus=0), dict(num_cus=12), dict(num_cus=264), dict(num_cus=-8),
+                                 dict(num_cus=256, exclude=True), dict(cu_count=250, num_cus=8)])
+def test_cu_mask_rejects(lib, bad):
+    args = dict(cu_count=256, exclude=False)
+    args.update(bad)
+    with pytest.raises(ep.EpError) as e:
+        ep.ep_cu_mask(args["cu_count"], args["num_cus"], args["exclude"])
+    assert e.value.code == ep.EP_ERR_ARG
+    assert lib.ep_stream_create_cus(8, 0, None) == ep.EP_ERR_ARG
+    assert lib.ep_cu_census(-1, 0, None, None) == ep.EP_ERR_ARG
+    assert lib.ep_stream_destroy(None) == ep.EP_OK
