@@ -70,6 +70,8 @@ def _bind(lib):
     lib.oracle_layout_dedup.argtypes = [i, i, i, i, ll, P, P, P]
     lib.oracle_positions_dedup.restype = None
     lib.oracle_positions_dedup.argtypes = [i, i, i, i, ll, P, P, P, P]
+    lib.oracle_ll_positions.restype = ctypes.c_uint32
+    lib.oracle_ll_positions.argtypes = [i, i, i, i, P, P, P, P]
     lib.oracle_dispatch_dedup.restype = None
     lib.oracle_dispatch_dedup.argtypes = [i, i, i, i, i, i, P, P, P, P, P, i, P, P, P, P]
     for name in ("oracle_e4m3_encode", "oracle_e4m3_decode", "oracle_bf16_round"):
@@ -250,6 +252,19 @@ class Oracle:
         rows = np.zeros(R, np.int32)
         st = int(self.lib.oracle_layout_dedup(T, k, E, R, int(cap_rows), _ptr(topk_idx), _ptr(rir), _ptr(rows)))
         return rir, rows, st
+
+    def ll_positions(self, topk_idx: np.ndarray, E: int, R: int):
+        """Low-latency receive layout. Returns (pos [T,k], src_idx [E*T],
+        recv_count [E,R], status); the rows themselves come from dispatch()
+        with these positions."""
+        topk_idx = _c(topk_idx, np.int32)
+        T, k = topk_idx.shape
+        assert E % R == 0 and T % R == 0
+        pos = np.empty((T, k), np.int32)
+        src_idx = np.empty(E * T, np.int32)
+        cnt = np.empty((E, R), np.int32)
+        st = int(self.lib.oracle_ll_positions(T, k, E, R, _ptr(topk_idx), _ptr(pos), _ptr(src_idx), _ptr(cnt)))
+        return pos, src_idx, cnt, st
 
     def positions_dedup(self, topk_idx: np.ndarray, rank_in_rank: np.ndarray, E: int, R: int, cap_rows: int):
         """Returns (pos [T,k] int32, src_idx [R*cap_rows] int32, -1 where unused)."""

@@ -267,6 +267,40 @@ void oracle_positions(int T, int k, int E, int R, long long cap_rows,
 }
 
 /* ------------------------------------------------------------------------- */
+/* Low-latency receive layout (the low-latency kernels of the blog.hotdry.top
+ * DeepEP notes, section 1, and their decode setting: a fixed receive buffer,
+ * at most a few hundred tokens per rank, no count exchange before sending).
+ * Reading: expert e owns R regions of tpr = T/R rows, region s for source rank
+ * s, so a source can place its rows without knowing any other source's
+ * counts. A kept slot (t, j) of source s = t / tpr with expert e goes to row
+ *   e*R*tpr + s*tpr + (number of earlier tokens of source s routed to e),
+ * found here with one counter per (expert, source) while t ascends.
+ * pos[t][j] = -1 for a dropped slot; src_idx[row] = t (E*T entries, -1 where
+ * unused); recv_count[e][s] = rows used in region (e, s). Returns the status
+ * bits of the slots (bad / repeated ids); a region never overflows. */
+uint32_t oracle_ll_positions(int T, int k, int E, int R, const int32_t *topk_idx,
+                             int32_t *pos, int32_t *src_idx, int32_t *recv_count) {
+    uint32_t status = 0;
+    int tpr = T / R;
+    long long region = (long long)R * tpr; /* rows per expert */
+    for (long long i = 0; i < (long long)E * region; ++i) src_idx[i] = -1;
+    for (int i = 0; i < E * R; ++i) recv_count[i] = 0;
+    for (int t = 0; t < T; ++t) {
+        const int32_t *row = topk_idx + (size_t)t * k;
+        int s = t / tpr;
+        for (int j = 0; j < k; ++j) {
+            pos[(size_t)t * k + j] = -1;
+            if (!slot_is_valid(row, j, E, &status)) continue;
+            int e = row[j];
+            long long p = (long long)e * region + (long long)s * tpr + recv_count[e * R + s];
+            recv_count[e * R + s] += 1;
+            pos[(size_t)t * k + j] = (int32_t)p;
+            src_idx[p] = t;
+        }
+    }
+    return status;
+}
+
 /* Rank-deduplicated exchange: one received row per (token, destination rank)
  * instead of one per (token, expert). Reading (the pages' normal kernels send
  * a token once per rank; the row then carries which of that rank's experts

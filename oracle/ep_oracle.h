@@ -43,6 +43,9 @@ void oracle_quantize_token(int H, const uint16_t *x_row, uint8_t *q, float *scal
 uint32_t oracle_layout_dedup(int T, int k, int E, int R, long long cap_rows,
                              const int32_t *topk_idx, int32_t *rank_in_rank, int32_t *token_rows);
 
+uint32_t oracle_ll_positions(int T, int k, int E, int R, const int32_t *topk_idx,
+                             int32_t *pos, int32_t *src_idx, int32_t *recv_count);
+
 void oracle_positions_dedup(int T, int k, int E, int R, long long cap_rows,
                             const int32_t *topk_idx, const int32_t *rank_in_rank,
                             int32_t *pos, int32_t *src_idx);

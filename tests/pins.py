@@ -680,10 +680,105 @@ def pin_dedup_prereduce(orc):
     assert np.array_equal(y_dd, y_ref), "dedup + pre-reduction differs from the per-expert combine"
 
 
+def pin_ll_golden(orc):
+    g = golden("layout_by_hand.json")
+    topk = np.array(g["topk_idx"], np.int32)
+    E, R = g["E"], g["R"]
+    ll = g["low_latency"]
+    pos, src_idx, cnt, st = orc.ll_positions(topk, E, R)
+    assert np.array_equal(pos, np.array(ll["pos"])), pos
+    assert np.array_equal(cnt, np.array(ll["recv_count"])), cnt
+    assert st == ll["status"]
+    for t, row in enumerate(ll["pos"]):
+        for p in row:
+            if p >= 0:
+                assert src_idx[p] == t
+
+
+def brute_ll(topk, E, R):
+    """Low-latency rows counted directly from the definition, O(T^2 k)."""
+    T, k = topk.shape
+    tpr = T // R
+
+    def kept(t):
+        seen, out = set(), []
+        for j in range(k):
+            e = int(topk[t, j])
+            if 0 <= e < E and e not in seen:
+                out.append((j, e))
+            if 0 <= e < E:
+                seen.add(e)
+        return out
+
+    pos = np.full((T, k), -1, np.int32)
+    for t in range(T):
+        s = t // tpr
+        for j, e in kept(t):
+            before = sum(1 for u in range(s * tpr, t) if any(ee == e for _, ee in kept(u)))
+            pos[t, j] = e * R * tpr + s * tpr + before
+    return pos
+
+
+def pin_ll_bruteforce(orc):
+    """Brute force, and agreement with the per-expert layout: a region holds
+    cnt_se[s][e] rows, and a slot's row inside it is its rank among expert e's
+    rows less the rows of earlier sources (rank_in_expert - src_expert_off)."""
+    rng = np.random.default_rng(61)
+    for T, k, E, R in ((32, 4, 16, 4), (40, 6, 24, 8), (24, 8, 8, 2), (9, 3, 6, 3)):
+        topk = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32)
+        topk[rng.random((T, k)) < 0.15] = -1
+        topk[rng.random((T, k)) < 0.05] = E + 2
+        dup = rng.random(T) < 0.2
+        topk[dup, k - 1] = topk[dup, 0]
+        pos, src_idx, cnt, st = orc.ll_positions(topk, E, R)
+        assert np.array_equal(pos, brute_ll(topk, E, R)), (T, k, E, R)
+        L = orc.layout(topk, E, R, 1 << 30)
+        assert st == L.status
+        assert np.array_equal(cnt, L.cnt_se.T), "region counts != cnt_se"
+        tpr = T // R
+        for t in range(T):
+            s = t // tpr
+            for j in range(k):
+                p = pos[t, j]
+                assert (p >= 0) == (L.rank_in_expert[t, j] >= 0)
+                if p >= 0:
+                    e = topk[t, j]
+                    assert p - e * R * tpr - s * tpr == L.rank_in_expert[t, j] - L.src_expert_off[s, e]
+
+
+def pin_ll_invariants(orc):
+    """Rows are distinct, inside their (expert, source) region, fill each
+    region from its first row in ascending token order, and src_idx inverts
+    pos."""
+    rng = np.random.default_rng(62)
+    T, k, E, R = 256, 8, 64, 8
+    topk = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32)
+    topk[rng.random((T, k)) < 0.1] = -1
+    pos, src_idx, cnt, _ = orc.ll_positions(topk, E, R)
+    tpr = T // R
+    kept = pos[pos >= 0]
+    assert kept.size == len(set(kept.tolist())) == (topk >= 0).sum() == cnt.sum()
+    for t in range(T):
+        for j in range(k):
+            p = pos[t, j]
+            if p < 0:
+                continue
+            e, s = topk[t, j], t // tpr
+            base = e * R * tpr + s * tpr
+            assert base <= p < base + cnt[e, s] and src_idx[p] == t
+    used = src_idx.reshape(E, R, tpr)
+    for e in range(E):
+        for s in range(R):
+            toks = used[e, s, :cnt[e, s]]
+            assert (toks >= s * tpr).all() and (toks < (s + 1) * tpr).all() and (np.diff(toks) > 0).all()
+            assert (used[e, s, cnt[e, s]:] == -1).all()
+
+
 ALL_PINS = [
     pin_e4m3_decode, pin_e4m3_encode, pin_bf16_round,
     pin_layout_golden, pin_layout_bruteforce, pin_layout_argsort, pin_layout_invariants,
     pin_dispatch_bf16, pin_fp8_golden, pin_fp8_bound, pin_fp8_torch,
     pin_combine_fp64, pin_combine_order, pin_combine_fma, pin_combine_identity, pin_backward,
     pin_dedup_golden, pin_dedup_bruteforce, pin_dedup_dispatch, pin_dedup_prereduce,
+    pin_ll_golden, pin_ll_bruteforce, pin_ll_invariants,
 ]

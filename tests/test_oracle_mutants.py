@@ -68,6 +68,15 @@ MUTANTS = [
     ("combine drops the last slot",
      "        for (int j = 0; j < k; ++j) {\n            int32_t p = pos[(size_t)t * k + j];\n            if (p < 0) continue;\n            float wt",
      "        for (int j = 0; j < k - 1; ++j) {\n            int32_t p = pos[(size_t)t * k + j];\n            if (p < 0) continue;\n            float wt"),
+    # low-latency receive layout
+    ("low-latency rows counted over all sources",
+     "long long p = (long long)e * region + (long long)s * tpr + recv_count[e * R + s];",
+     "long long p = (long long)e * region + (long long)s * tpr + recv_count[e * R] * (s == 0);"),
+    ("low-latency region stride per source wrong",
+     "long long p = (long long)e * region + (long long)s * tpr + recv_count[e * R + s];",
+     "long long p = (long long)e * region + (long long)s * (tpr - 1) + recv_count[e * R + s];"),
+    ("low-latency source of a token off by one", "        int s = t / tpr;\n        for (int j = 0; j < k; ++j) {\n            pos[(size_t)t * k + j] = -1;",
+     "        int s = (t + 1) / tpr % R;\n        for (int j = 0; j < k; ++j) {\n            pos[(size_t)t * k + j] = -1;"),
     # rank-deduplicated exchange
     ("dedup leader by expert instead of rank",
      "if (slot_is_valid(row, jj, E, &ignore) && row[jj] / experts_per_rank == d) leader = 0;",
