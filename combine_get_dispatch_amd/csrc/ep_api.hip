@@ -407,6 +407,40 @@ int ep_dispatch_dedup(ep_ctx *ctx, const uint16_t *x, const int32_t *topk_idx, c
                            handle, stream, "ep_dispatch_dedup", recv_topk_idx, recv_topk_w);
 }
 
+int ep_dispatch_low_latency(ep_ctx *ctx, const uint16_t *x, const int32_t *topk_idx, const float *topk_weights,
+                            int use_fp8, void *recv_x, float *recv_scales, float *recv_w, int32_t *recv_count,
+                            ep_handle *handle, ep_stream_t stream) {
+    if (!ctx || !handle || !recv_count) return EP_ERR_ARG;
+    const ep_config &c = ctx->cfg;
+    const int T = c.num_tokens, R = c.num_ranks;
+    if (use_fp8 != 0 && use_fp8 != 1) return EP_ERR_ARG;
+    if (use_fp8 && (c.hidden % 128 || !recv_scales)) return EP_ERR_ARG;
+    if (!use_fp8 && recv_scales) return EP_ERR_ARG;
+    // the low-latency receive layout: every expert holds T rows (R regions of T/R)
+    if (c.cap_rows * R != (int64_t)c.num_experts * T || T / R > ep::kLayoutTile) return EP_ERR_ARG;
+    if (T > 0 && (!topk_idx || !handle->pos || !handle->src_idx)) return EP_ERR_ARG;
+    if (!aligned(recv_count, 4) || !aligned(topk_idx, 4) || !aligned(topk_weights, 4) || !aligned(recv_w, 4) ||
+        !aligned(recv_scales, 4) || !aligned(handle->src_idx, 4))
+        return EP_ERR_ALIGN;
+    handle->num_tokens = T;
+    handle->num_topk = c.num_topk;
+    ep::DispatchArgs a;
+    if (T == 0) {  // the region counts only
+        std::memset(&a, 0, sizeof a);
+        a.E = c.num_experts;
+        a.k = c.num_topk;
+        a.waves_per_token = 1;
+        return hip_fail(ep::launch_ll_dispatch(a, false, R, recv_count, (hipStream_t)stream),
+                        "ep_dispatch_low_latency");
+    }
+    Geometry g;
+    if (int r = fill_dispatch(ctx, x, topk_idx, topk_weights, nullptr, 0, recv_x, recv_scales, recv_w, handle, a,
+                              g))
+        return r;
+    return hip_fail(ep::launch_ll_dispatch(a, use_fp8 != 0, R, recv_count, (hipStream_t)stream),
+                    "ep_dispatch_low_latency");
+}
+
 int ep_dispatch_with_layout(ep_ctx *ctx, const uint16_t *x, const int32_t *topk_idx, const float *topk_weights,
                             const ep_layout *L, int use_fp8, void *recv_x, float *recv_scales, float *recv_w,
                             ep_handle *handle, ep_stream_t stream) {

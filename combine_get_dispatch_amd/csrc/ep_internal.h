@@ -90,5 +90,8 @@ int layout_dispatch_blocks_per_cu(int k, bool fp8, size_t lds);
 hipError_t launch_combine(const CombineArgs &a, bool out_f32, int num_waves, hipStream_t s);
 hipError_t launch_copy(const void *src, void *dst, size_t n16, hipStream_t s);
 hipError_t launch_cu_census(int blocks, int naps, uint32_t *ids, hipStream_t s);
+// low-latency dispatch: a.T % R == 0, a.T / R <= kLayoutTile, rows e*T + s*(T/R) + r
+size_t ll_lds_bytes(int E, int k, int tpr);
+hipError_t launch_ll_dispatch(const DispatchArgs &a, bool fp8, int R, int32_t *recv_count, hipStream_t s);
 
 }  // namespace ep

@@ -17,6 +17,8 @@
 //               multiply-add per slot in slot order, then rounds to bf16.
 //   k_copy      plain 128-bit streaming copy (bandwidth calibration).
 //   k_cu_census the compute unit each workgroup runs on (checks stream CU masks).
+//   k_ll_dispatch low-latency dispatch: fixed per-(expert, source) regions, no
+//               look-back, every block self-contained.
 //
 // The operations follow the DeepEP usage guide's dispatch / combine /
 // backward interface (zhouruolin.cn DeepEP guide, section 5); the arithmetic
@@ -927,6 +929,106 @@ __global__ __launch_bounds__(kTileTokens) void k_dispatch_inblock(LayoutArgs la,
     store_rows<FP8>(da, part, p, v);
 }
 
+// Low-latency dispatch. Expert e's rows are R regions of tpr = T/R rows, one
+// per source rank, so the row of a slot depends only on the tokens of its own
+// source: slot (t, j) of source s with expert e lands in row
+// e*R*tpr + s*tpr + (earlier tokens of s routed to e). Block b serves source
+// s = b / bps: one thread per token of the source (tpr <= 256) validates its
+// slots and ORs its bit into a per-wave 64-bit token mask of each of its
+// experts in LDS; after one barrier every wave counts its slots' ranks with
+// popcounts and writes its rows. No block waits on another and the context
+// workspace is not used. The first block of each source writes the region
+// counts recv_count[e][s].
+template <int KMAX, bool FP8>
+__global__ __launch_bounds__(kTileTokens) void k_ll_dispatch(DispatchArgs da, int R, int tpr, int bps,
+                                                            int32_t *__restrict__ recv_count) {
+    extern __shared__ uint64_t ll_lds[];
+    if (tpr == 0) {  // no tokens: empty regions
+        for (int i = threadIdx.x; i < da.E * R; i += kTileTokens) recv_count[i] = 0;
+        return;
+    }
+    const int nw = (tpr + 63) >> 6;                                   // waves holding the source's tokens
+    uint64_t *masks = ll_lds;                                         // [nw][E] token bits per expert
+    int *slots = reinterpret_cast<int *>(ll_lds + (size_t)nw * da.E);  // [tpr][k] kept expert or -1
+    const int s = blockIdx.x / bps, bi = blockIdx.x - s * bps;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int item = bi * kWavesPerBlock + wave;
+    const int tl = item / da.waves_per_token, part = item - tl * da.waves_per_token;
+    const bool active = tl < tpr;  // whole wave
+    const int t = s * tpr + (active ? tl : 0);
+    // loads before any store: the source's slots (thread tid = its token tid),
+    // the slot weight, then the rows
+    int raw[KMAX];
+    {
+        const int32_t *row = da.topk + (size_t)(s * tpr + min(tid, tpr - 1)) * da.k;
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) raw[j] = row[min(j, da.k - 1)];
+    }
+    const float wslot = (active && part == 0 && lane < da.k && da.recv_w) ? da.w[(size_t)t * da.k + lane] : 0.0f;
+    u32x4 v[2 * kMaxPassPerWave];
+    load_rows<FP8>(da, t, part, active, v);
+    for (int i = tid; i < nw * da.E; i += kTileTokens) masks[i] = 0;
+    uint32_t st = 0;
+    int ev[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+        ev[j] = -1;
+        if (tid >= tpr || j >= da.k) continue;
+        const int e = raw[j];
+        if (e == -1) continue;
+        if (e < 0 || e >= da.E) {
+            st |= kStBad;
+            continue;
+        }
+        bool dup = false;
+#pragma unroll
+        for (int jj = 0; jj < j; ++jj) dup |= raw[jj] == e;
+        if (dup) {
+            st |= kStDup;
+            continue;
+        }
+        ev[j] = e;
+    }
+    __syncthreads();  // masks cleared
+    const uint64_t bit = 1ull << lane;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j)
+        if (ev[j] >= 0) atomicOr(reinterpret_cast<unsigned long long *>(masks + wave * da.E + ev[j]), bit);
+    if (tid < tpr) {
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j)
+            if (j < da.k) slots[tid * da.k + j] = ev[j];
+    }
+    if (st && bi == 0) atomicOr(&da.counters[kStatus], st);
+    __syncthreads();  // masks and slots complete
+    if (bi == 0)
+        for (int e = tid; e < da.E; e += kTileTokens) {
+            int c = 0;
+            for (int w = 0; w < nw; ++w) c += __popcll(masks[w * da.E + e]);
+            recv_count[(size_t)e * R + s] = c;
+        }
+    if (!active) return;
+    int p = -1;
+    if (lane < da.k) {
+        const int e = slots[tl * da.k + lane];
+        if (e >= 0) {
+            const int w0 = tl >> 6;
+            int r = __popcll(masks[w0 * da.E + e] & ((1ull << (tl & 63)) - 1));
+            for (int w = 0; w < w0; ++w) r += __popcll(masks[w * da.E + e]);
+            p = (int)((int64_t)e * R * tpr + (int64_t)s * tpr + r);
+        }
+        if (part == 0) {
+            const size_t i = (size_t)t * da.k + lane;
+            da.pos[i] = p;
+            if (p >= 0) {
+                da.src_idx[p] = t;
+                if (da.recv_w) da.recv_w[p] = wslot;
+            }
+        }
+    }
+    store_rows<FP8>(da, part, p, v);
+}
+
 // The dispatch side of a fused grid with flags: the block's NW waves load
 // (and, for FP8, later quantize) their rows before the layout is known, wait
 // for the layout blocks of their tokens and for the totals, then write the
@@ -1275,6 +1377,27 @@ hipError_t launch_combine(const CombineArgs &a, bool out_f32, int num_waves, hip
 
 hipError_t launch_cu_census(int blocks, int naps, uint32_t *ids, hipStream_t s) {
     hipLaunchKernelGGL(k_cu_census, dim3(blocks), dim3(64), 0, s, ids, naps);
+    return hipGetLastError();
+}
+
+size_t ll_lds_bytes(int E, int k, int tpr) { return (size_t)((tpr + 63) / 64) * E * 8 + (size_t)tpr * k * 4; }
+
+hipError_t launch_ll_dispatch(const DispatchArgs &a, bool fp8, int R, int32_t *recv_count, hipStream_t s) {
+    const int tpr = a.T / R;
+    const int bps = (tpr * a.waves_per_token + kWavesPerBlock - 1) / kWavesPerBlock;
+    const dim3 grid(max(R * bps, 1)), block(kTileTokens);
+    const size_t lds = ll_lds_bytes(a.E, a.k, tpr);
+    if (a.k <= 8) {
+        if (fp8)
+            hipLaunchKernelGGL((k_ll_dispatch<8, true>), grid, block, lds, s, a, R, tpr, bps, recv_count);
+        else
+            hipLaunchKernelGGL((k_ll_dispatch<8, false>), grid, block, lds, s, a, R, tpr, bps, recv_count);
+    } else {
+        if (fp8)
+            hipLaunchKernelGGL((k_ll_dispatch<kMaxTopk, true>), grid, block, lds, s, a, R, tpr, bps, recv_count);
+        else
+            hipLaunchKernelGGL((k_ll_dispatch<kMaxTopk, false>), grid, block, lds, s, a, R, tpr, bps, recv_count);
+    }
     return hipGetLastError();
 }
 

@@ -78,6 +78,9 @@ SIGNATURES = {
     "ep_dispatch_dedup": (ctypes.c_int, [c_void_p, c_void_p, c_void_p, c_void_p, ctypes.POINTER(EpLayout),
                                          ctypes.c_int, c_void_p, c_void_p, c_void_p, c_void_p,
                                          ctypes.POINTER(EpHandle), c_void_p]),
+    "ep_dispatch_low_latency": (ctypes.c_int, [c_void_p, c_void_p, c_void_p, c_void_p, ctypes.c_int, c_void_p,
+                                               c_void_p, c_void_p, c_void_p, ctypes.POINTER(EpHandle),
+                                               c_void_p]),
     "ep_combine": (ctypes.c_int, [c_void_p, c_void_p, ctypes.POINTER(EpHandle), c_void_p, c_void_p,
                                   c_void_p]),
     "ep_combine_f32": (ctypes.c_int, [c_void_p, c_void_p, ctypes.POINTER(EpHandle), c_void_p,
@@ -182,6 +185,20 @@ def ep_dispatch_dedup(ctx: int, x: int, topk_idx: int, topk_weights: Optional[in
                                     stream), "ep_dispatch_dedup")
 
 
+def ep_dispatch_low_latency(ctx: int, x: int, topk_idx: int, topk_weights: Optional[int], use_fp8: int,
+                            recv_x: int, recv_scales: Optional[int], recv_w: Optional[int], recv_count: int,
+                            handle: EpHandle, stream: int) -> None:
+    _check(load().ep_dispatch_low_latency(ctx, x, topk_idx, topk_weights, int(use_fp8), recv_x, recv_scales,
+                                          recv_w, recv_count, ctypes.byref(handle), stream),
+           "ep_dispatch_low_latency")
+
+
+def ll_cap_rows(num_tokens: int, num_experts: int, num_ranks: int) -> int:
+    """cap_rows of a context for the low-latency receive layout: every expert
+    holds num_tokens rows (one region of num_tokens/num_ranks per source)."""
+    return num_experts * num_tokens // num_ranks
+
+
 def ep_combine(ctx: int, expert_out: int, handle: EpHandle, weights: Optional[int],
                combined_x: int, stream: int) -> None:
     _check(load().ep_combine(ctx, expert_out, ctypes.byref(handle), weights, combined_x, stream),
@@ -283,6 +300,14 @@ class Handle:
         return EpHandle(self.pos.data_ptr(), self.src_idx.data_ptr(), self.num_tokens, self.num_topk)
 
 
+_deferred_contexts = []
+
+
+def _destroy_deferred() -> None:
+    while _deferred_contexts:
+        ep_destroy(_deferred_contexts.pop())
+
+
 class Buffer:
     """One expert-parallel group collapsed onto the current GPU: the analogue
     of the DeepEP guide's buffer (created once for a token count, hidden size
@@ -295,6 +320,7 @@ class Buffer:
         self.device = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
         self.cfg = EpConfig(num_tokens, num_topk, num_experts, num_ranks, hidden, 0, int(cap_rows))
         self.sizes = ep_query_sizes(self.cfg)
+        _destroy_deferred()
         with torch.cuda.device(self.device):
             self.ctx = ep_create(self.cfg)
 
@@ -321,8 +347,15 @@ class Buffer:
     def num_rows(self): return self.R * self.cap_rows
 
     def close(self):
+        """Destroy the context (ep_destroy synchronizes the device, which a
+        HIP graph capture forbids: a buffer released while a capture is in
+        progress is destroyed by the next close or new buffer instead)."""
         if getattr(self, "ctx", None):
-            ep_destroy(self.ctx)
+            if self.torch.cuda.is_current_stream_capturing():
+                _deferred_contexts.append(self.ctx)
+            else:
+                _destroy_deferred()
+                ep_destroy(self.ctx)
             self.ctx = None
 
     def __del__(self):
@@ -409,6 +442,26 @@ class Buffer:
                           _ptr(recv_topk_w), ch, _stream())
         handle.num_tokens, handle.num_topk = ch.num_tokens, ch.num_topk
         return recv_x, recv_scales, recv_topk_idx, recv_topk_w, handle
+
+    def dispatch_low_latency(self, x, topk_idx, topk_weights, use_fp8: bool, out=None):
+        """Low-latency dispatch (the buffer must have cap_rows =
+        ll_cap_rows(T, E, R)). Returns (recv_x, recv_scales, recv_w,
+        recv_count [E, R], handle)."""
+        t = self.torch
+        if out is None:
+            recv_x = self._empty((self.num_rows, self.H), t.uint8 if use_fp8 else t.bfloat16)
+            recv_scales = self._empty((self.num_rows, self.H // 128), t.float32) if use_fp8 else None
+            recv_w = self._empty(self.num_rows, t.float32) if topk_weights is not None else None
+            recv_count = self._empty((self.E, self.R), t.int32)
+            handle = self.new_handle()
+        else:
+            recv_x, recv_scales, recv_w, recv_count, handle = out
+        ch = handle.c()
+        ep_dispatch_low_latency(self.ctx, x.data_ptr(), topk_idx.data_ptr(), _ptr(topk_weights),
+                                int(bool(use_fp8)), recv_x.data_ptr(), _ptr(recv_scales), _ptr(recv_w),
+                                recv_count.data_ptr(), ch, _stream())
+        handle.num_tokens, handle.num_topk = ch.num_tokens, ch.num_topk
+        return recv_x, recv_scales, recv_w, recv_count, handle
 
     def combine(self, expert_out, handle: Handle, weights=None, out=None):
         out = out if out is not None else self._empty((self.T, self.H), self.torch.bfloat16)

@@ -139,7 +139,8 @@ int ep_query_sizes(const ep_config *cfg, ep_sizes *out);
  * success. Returns EP_OK, EP_ERR_ARG, EP_ERR_NOMEM or EP_ERR_HIP. */
 int ep_create(const ep_config *cfg, ep_ctx **out);
 
-/* Free the workspace (synchronizes the device first). NULL is ignored. */
+/* Free the workspace (synchronizes the device first, so it must not be
+ * called while a HIP graph capture is in progress). NULL is ignored. */
 int ep_destroy(ep_ctx *ctx);
 
 /* Dispatch layout from top-k routing (the step before the guide's dispatch;
@@ -211,6 +212,25 @@ int ep_dispatch_dedup(ep_ctx *ctx, const uint16_t *x, const int32_t *topk_idx,
                       const float *topk_weights, const ep_layout *layout, int use_fp8,
                       void *recv_x, float *recv_scales, int32_t *recv_topk_idx, float *recv_topk_w,
                       ep_handle *handle, ep_stream_t stream);
+
+/* Low-latency dispatch (the low-latency kernels of the DeepEP notes, section
+ * 1: decode batches, a receive buffer fixed in advance, no count exchange;
+ * section 5: at most 256 tokens per rank). One launch, no layout call, no
+ * workspace and no block waiting on another, so it can be captured in a HIP
+ * graph as it is. Receive layout: expert e owns R regions of T/R rows, region
+ * s for source rank s, so rank d's rows [d*cap_rows, (d+1)*cap_rows) hold its
+ * experts' regions in ascending expert order. A kept slot (t, j) of source
+ * s = t / (T/R) with expert e goes to row
+ *   pos[t][j] = e*T + s*(T/R) + (earlier tokens of source s routed to e)
+ * (-1 for an empty, bad or repeated slot: status bits as for the layout),
+ * src_idx[pos] = t; the row, scales and recv_w as in ep_dispatch.
+ * recv_count: [E][R] int32, rows used in region (e, s) (required).
+ * Requires cap_rows * R == E * T (every expert holds T rows) and T/R <= 256;
+ * else EP_ERR_ARG. The handle works with ep_combine, ep_combine_backward and
+ * ep_dispatch_backward. Rows past a region's count are not written. */
+int ep_dispatch_low_latency(ep_ctx *ctx, const uint16_t *x, const int32_t *topk_idx,
+                            const float *topk_weights, int use_fp8, void *recv_x, float *recv_scales,
+                            float *recv_w, int32_t *recv_count, ep_handle *handle, ep_stream_t stream);
 
 /* Combine (the guide's combine): weighted gather-reduce back to source-token
  * order. For each token t and channel i: acc = +0.0f; for j = 0..k-1 with

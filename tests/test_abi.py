@@ -134,3 +134,8 @@ def test_cu_mask_rejects(lib, bad):
     assert lib.ep_stream_create_cus(8, 0, None) == ep.EP_ERR_ARG
     assert lib.ep_cu_census(-1, 0, None, None) == ep.EP_ERR_ARG
     assert lib.ep_stream_destroy(None) == ep.EP_OK
+
+
+def test_low_latency_rejects_other_receive_sizes(lib):
+    assert lib.ep_dispatch_low_latency(None, None, None, None, 0, None, None, None, None, None, None) == ep.EP_ERR_ARG
+    assert ep.ll_cap_rows(1024, 256, 8) == 32768  # every expert holds T rows: R*cap_rows = E*T

@@ -3,6 +3,7 @@ seeded inputs. Integer, index and byte outputs (layout, positions, source
 indices, FP8 codes, scales, copied rows, weights) must be bit-exact; the bf16
 combine must be within 1 bf16 ulp of the oracle (same fp32 FMA order, so 0 is
 expected) and its fp32 sums within 1e-6 relative (bit-exact expected)."""
+import gc
 from dataclasses import replace
 
 import numpy as np
@@ -445,6 +446,8 @@ def test_graph_replay_matches_eager(fused, cfg_name):
     rows = torch.from_numpy(used_rows(host(out[3].pos)).astype(np.int64)).cuda()
     ref = [host(L.rank_in_expert), host(out[3].pos), out[0].index_select(0, rows).cpu().numpy(),
            out[1].index_select(0, rows).cpu().numpy(), host_u16(y)]
+    gc.collect()  # no buffer of an earlier test may be released during the capture
+    torch.cuda.synchronize()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
