@@ -116,6 +116,33 @@ class Path:
         return int((self.handle.pos >= 0).sum().item())
 
 
+class LlPath:
+    """The low-latency form of a workload's step: one dispatch launch into
+    fixed per-(expert, source) regions, then combine on its handle."""
+
+    def __init__(self, main, torch, ep, workloads, seed):
+        cfg = main.cfg
+        self.main = main
+        self.buf = ep.Buffer(cfg.T, cfg.H, cfg.k, cfg.E, cfg.R, ep.ll_cap_rows(cfg.T, cfg.E, cfg.R))
+        n = self.buf.num_rows
+        self.recv_x = torch.empty((n, cfg.H), dtype=torch.uint8 if cfg.use_fp8 else torch.bfloat16, device="cuda")
+        self.recv_scales = torch.empty((n, cfg.H // 128), dtype=torch.float32, device="cuda") if cfg.use_fp8 else None
+        self.recv_w = torch.empty(n, dtype=torch.float32, device="cuda")
+        self.recv_count = torch.empty((cfg.E, cfg.R), dtype=torch.int32, device="cuda")
+        self.handle = self.buf.new_handle()
+        self.expert_out = workloads.device_normal_bf16((n, cfg.H), seed=seed + 404)
+        self.y = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device="cuda")
+
+    def dispatch_op(self):
+        m = self.main
+        self.buf.dispatch_low_latency(m.x, m.topk, m.w, m.cfg.use_fp8,
+                                      out=(self.recv_x, self.recv_scales, self.recv_w, self.recv_count,
+                                           self.handle))
+
+    def combine_op(self):
+        self.buf.combine(self.expert_out, self.handle, self.main.w, out=self.y)
+
+
 def dedup_bytes(T, k, H, Nd, use_fp8):
     """Algorithmic bytes of the rank-deduplicated step (Nd = rows, one per
     (token, destination rank)): dispatch reads x and the weights, writes the
@@ -680,17 +707,32 @@ def main():
             dms, (ld_, c_) = timed(torch, ops2, max(K, 100), W)
             dst_ = dp.buf.status()
             dd, dc, _ = algo_bytes(dp.cfg.T, dp.cfg.k, dp.cfg.H, dp.kept_slots(), True)
+            lp = LlPath(dp, torch, ep, workloads, args.seed)
+            ll_ops = [lp.dispatch_op, lp.combine_op]
+            ll_us, _ = graph_timed(torch, ll_ops, max(K, 200), W)
+            _, (lld_, llc_) = timed(torch, ll_ops, max(K, 100), W)
+            ll_st = lp.buf.status()
+            lp.buf.close()
+            del lp
             dec[name] = {"tokens": dp.cfg.T, "us_per_step_graph": round(g_us, 2),
                          "us_per_step_graph_wall": round(g_wall, 2),
                          "GBps_graph": round((dd + dc) / (g_us * 1e-6) / 1e9, 1),
                          "us_per_step_graph_three_launches": round(g3_us, 2),
                          "us_per_step_eager": round(dms * 1e3, 2),
                          "eager_layout_dispatch_us": round(ld_ * 1e3, 2),
-                         "eager_combine_us": round(c_ * 1e3, 2), "status": dst_}
+                         "eager_combine_us": round(c_ * 1e3, 2), "status": dst_,
+                         "low_latency": {"us_per_step_graph": round(ll_us, 2),
+                                         "GBps_graph": round((dd + dc) / (ll_us * 1e-6) / 1e9, 1),
+                                         "eager_dispatch_us": round(lld_ * 1e3, 2),
+                                         "eager_dispatch_GBps": round(dd / (lld_ * 1e-3) / 1e9, 1),
+                                         "eager_combine_us": round(llc_ * 1e3, 2), "status": ll_st}}
             dp.buf.close()
             del dp
         out["decode"] = dec
-        out["us_at_128_tokens"] = dec["decode_rank"]["us_per_step_graph"]
+        # the pages' decode setting runs their low-latency kernels: the
+        # headline latency is that path's (the normal path's is beside it)
+        out["us_at_128_tokens"] = dec["decode_rank"]["low_latency"]["us_per_step_graph"]
+        out["us_at_128_tokens_normal_path"] = dec["decode_rank"]["us_per_step_graph"]
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(main_path, args.cpu_seconds)
