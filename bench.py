@@ -47,6 +47,12 @@ def parse():
     p.add_argument("--separate", action="store_true",
                    help="time the step as three calls (layout, dispatch, combine) instead of the fused "
                         "layout+dispatch launch followed by combine")
+    p.add_argument("--ll", action="store_true",
+                   help="time the low-latency form as the step (one dispatch launch into fixed "
+                        "per-(expert, source) regions, then combine); implies --no-extras")
+    p.add_argument("--dedup", action="store_true",
+                   help="time the rank-deduplicated form as the step (layout, one row per (token, rank), "
+                        "combine of the pre-reduced rows); implies --no-extras")
     p.add_argument("--record-traffic", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "TRACE_DIR"),
                    help="summarize rocprofv3 runs of this bench (--pmc FETCH_SIZE, --pmc WRITE_SIZE, "
                         "--kernel-trace --stats, all with --output-format csv) into profiles/")
@@ -406,7 +412,8 @@ def measured_traffic(kernel, workload):
 # rocprofv3 summaries -> profiles/
 # ---------------------------------------------------------------------------
 
-KERNELS = {"k_layout": "k_layout<", "k_layout_dispatch": "k_layout_dispatch<", "k_dispatch": "k_dispatch<true, true>",
+KERNELS = {"k_layout": "k_layout<", "k_layout_dispatch": "k_layout_dispatch<", "k_dispatch": "k_dispatch<true, 1>",
+           "k_dispatch_dedup": "k_dispatch<true, 2>", "k_ll_dispatch": "k_ll_dispatch<",
            "k_combine": "k_combine<false>", "k_copy": "k_copy"}
 
 
@@ -432,6 +439,15 @@ def _per_kernel(rows, value_key):
     return out
 
 
+def traffic_key(cfg, args):
+    return cfg.name + ("_low_latency" if args.ll else "_dedup" if args.dedup else
+                       "_separate" if args.separate else "")
+
+
+def mode_flags(args):
+    return "".join(f" --{n}" for n in ("ll", "dedup", "separate") if getattr(args, n))
+
+
 def record_traffic(args, cfg, nb_copy):
     fetch = _per_kernel(_csv_rows(args.record_traffic[0], "counter_collection.csv"), "Counter_Value")
     write = _per_kernel(_csv_rows(args.record_traffic[1], "counter_collection.csv"), "Counter_Value")
@@ -444,11 +460,13 @@ def record_traffic(args, cfg, nb_copy):
     res = {"source_sha": source_sha(), "workload": cfg.name,
            "calibration": {"copy_bytes_each_way": nb_copy, "FETCH_SIZE_bytes": f_copy, "WRITE_SIZE_bytes": w_copy,
                            "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)}}
-    for k in ("k_layout_dispatch", "k_layout", "k_dispatch", "k_combine"):
-        # main-loop launches in order (the layout's first launch sizes the buffers)
+    for k in [k for k in KERNELS if k != "k_copy"]:
+        # the first n launches in order (the layout's first launch sizes the buffers)
         first = 1 if k == "k_layout" else 0
         fs = [v for g, v in fetch[k]][first:first + n]
         ws = [v for g, v in write[k]][first:first + n]
+        if not fs or len(fs) != len(ws):
+            continue
         fb, wb = mean(fs) * 1024.0 * f_scale, mean(ws) * 1024.0 * w_scale
         res[k] = {"launches": len(fs), "fetch_bytes": round(fb), "write_bytes": round(wb),
                   "hbm_bytes_per_launch": round(fb + wb)}
@@ -459,21 +477,23 @@ def record_traffic(args, cfg, nb_copy):
             allres = json.load(f)
     except (OSError, ValueError):
         allres = {}
-    allres[cfg.name] = res
+    allres[traffic_key(cfg, args)] = res
     with open(path, "w") as f:
         json.dump(allres, f, indent=1)
     return res, trace
 
 
 def write_profile_summaries(args, cfg, res, trace, algo):
-    cmd_bench = f"python3 bench.py --config {cfg.name} --steps {args.steps} --warmup {args.warmup} --no-cpu-baseline --no-decode"
+    ll = mode_flags(args)
+    cmd_bench = (f"python3 bench.py --config {cfg.name}{ll} --steps {args.steps} --warmup {args.warmup} "
+                 "--no-cpu-baseline --no-decode" + (" --no-extras" if args.no_extras and not (args.ll or args.dedup) else ""))
     lines = [f"# {cfg.name}: kernel trace and HBM traffic (rocprofv3)", "",
              f"Workload: {cfg.desc}.", "",
              "Commands (run from /tmp with TMPDIR=/tmp; the bench runs from the repository root):", "",
              f"    rocprofv3 --kernel-trace --stats --output-format csv -d <trace> -o run -- {cmd_bench}",
              f"    rocprofv3 --pmc FETCH_SIZE --output-format csv -d <fetch> -o run -- {cmd_bench}",
              f"    rocprofv3 --pmc WRITE_SIZE --output-format csv -d <write> -o run -- {cmd_bench}",
-             f"    python3 bench.py --config {cfg.name} --steps {args.steps} --warmup {args.warmup} "
+             f"    python3 bench.py --config {cfg.name}{ll} --steps {args.steps} --warmup {args.warmup} "
              "--record-traffic <fetch> <write> <trace>", "",
              "## Kernel statistics (--kernel-trace --stats)", "",
              "| kernel | calls | avg us | min us | max us | share % |", "|---|---|---|---|---|---|"]
@@ -489,7 +509,7 @@ def write_profile_summaries(args, cfg, res, trace, algo):
               f"for it, so the counters are scaled by {c['fetch_scale']} and {c['write_scale']}.", "",
               "| kernel | launches | fetch MB | write MB | HBM MB | algorithmic MB | HBM / algorithmic |",
               "|---|---|---|---|---|---|---|"]
-    for k in ("k_layout_dispatch", "k_layout", "k_dispatch", "k_combine"):
+    for k in [k for k in KERNELS if k in res]:
         e = res[k]
         a = algo.get(k)
         ratio = f"{e['hbm_bytes_per_launch'] / a:.3f}" if a else "-"
@@ -497,7 +517,7 @@ def write_profile_summaries(args, cfg, res, trace, algo):
         lines.append(f"| `{k}` | {e['launches']} | {e['fetch_bytes'] / 1e6:.1f} | {e['write_bytes'] / 1e6:.1f} | "
                      f"{e['hbm_bytes_per_launch'] / 1e6:.1f} | {amb} | {ratio} |")
     lines += ["", f"Kernel sources: sha256 prefix {res['source_sha']} (ep_kernels.hip, ep_api.hip, ep_internal.h)."]
-    with open(os.path.join(PROFILES, f"{cfg.name}_kernels_and_traffic.md"), "w") as f:
+    with open(os.path.join(PROFILES, f"{traffic_key(cfg, args)}_kernels_and_traffic.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
 
 
@@ -536,6 +556,10 @@ def cpu_baseline(path, seconds):
 
 def main():
     args = parse()
+    if args.ll and args.dedup:
+        raise SystemExit("bench.py: --ll and --dedup are two different steps; pick one")
+    if args.ll or args.dedup:
+        args.no_extras = True
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (--gpus {args.gpus} requested); "
               "the multi-GPU exchange is not part of it.", file=sys.stderr)
@@ -545,11 +569,21 @@ def main():
     K, W = args.steps, args.warmup
     if args.record_traffic:
         # no GPU work: summarize the profiler output of an earlier run of this bench
+        import numpy as np
         wl = workloads.make_workload(cfg, seed=args.seed, with_x=False)
         N = int((wl.topk_idx >= 0).sum())
         d_b, c_b, _ = algo_bytes(cfg.T, cfg.k, cfg.H, N, cfg.use_fp8)
-        res, trace = record_traffic(args, cfg, (c_b // 2) // 16 * 16)
-        write_profile_summaries(args, cfg, res, trace, {"k_layout_dispatch": d_b, "k_dispatch": d_b, "k_combine": c_b})
+        # rows of the rank-deduplicated form: distinct (token, destination rank) pairs
+        epr = cfg.E // cfg.R
+        tk = wl.topk_idx
+        t_of = np.repeat(np.arange(cfg.T), cfg.k).reshape(tk.shape)
+        Nd = int(np.unique((t_of * cfg.R + tk // epr)[tk >= 0]).size)
+        dd_b, dc_b = dedup_bytes(cfg.T, cfg.k, cfg.H, Nd, cfg.use_fp8)
+        if args.dedup:  # the step's combine reads the deduplicated rows
+            c_b = dc_b
+        res, trace = record_traffic(args, cfg, (c_b // 2) // 16 * 16)  # the copy the bench ran
+        write_profile_summaries(args, cfg, res, trace, {"k_layout_dispatch": d_b, "k_dispatch": d_b, "k_combine": c_b,
+                                                        "k_ll_dispatch": d_b, "k_dispatch_dedup": dd_b})
         print(json.dumps(res))
         return
 
@@ -558,13 +592,20 @@ def main():
     ep.load()
     torch.cuda.set_device(0)
     main_path = Path(cfg, args.seed, torch, ep, workloads)
-    fused = not args.separate
-    main_ops = [main_path.fused_op, main_path.combine_op] if fused else \
-        [main_path.layout_op, main_path.dispatch_op, main_path.combine_op]
+    fused = not args.separate and not args.ll and not args.dedup
+    llp = LlPath(main_path, torch, ep, workloads, args.seed) if args.ll else None
+    dedp = DedupPath(main_path, torch, ep, workloads, args.seed) if args.dedup else None
+    if llp is not None:
+        main_ops = [llp.dispatch_op, llp.combine_op]
+    elif dedp is not None:
+        main_ops = [dedp.layout_op, dedp.dispatch_op, dedp.combine_op]
+    else:
+        main_ops = [main_path.fused_op, main_path.combine_op] if fused else \
+            [main_path.layout_op, main_path.dispatch_op, main_path.combine_op]
     # eager launches with events around every op: the per-kernel durations
     # (and the step itself with --eager)
     eager_ms, per_op = timed(torch, main_ops, K, W)
-    if fused:
+    if fused or llp is not None:
         ld_ms, com_ms = per_op
     else:
         lay_ms, dis_ms, com_ms = per_op
@@ -572,14 +613,22 @@ def main():
         ms, ms_events, per_graph = eager_ms, eager_ms, 0
     else:
         ms, ms_events, per_graph = graph_step_timed(torch, main_ops, K, W)
-    st = main_path.buf.status()
+    step_buf = llp.buf if llp is not None else dedp.buf if dedp is not None else main_path.buf
+    st = step_buf.status()
     if st:
         raise SystemExit(f"bench: device status {st} on {cfg.name}")
-    N = main_path.kept_slots()
+    if llp is not None:
+        N = int((llp.handle.pos >= 0).sum().item())
+    elif dedp is not None:
+        N = dedp.rows()
+    else:
+        N = main_path.kept_slots()
     d_bytes, c_bytes, cb_bytes = algo_bytes(cfg.T, cfg.k, cfg.H, N, cfg.use_fp8)
+    if dedp is not None:
+        d_bytes, c_bytes = dedup_bytes(cfg.T, cfg.k, cfg.H, N, cfg.use_fp8)
     value = (d_bytes + c_bytes) / (ms * 1e-3) / 1e9
     achieved = c_bytes / (com_ms * 1e-3) / 1e9
-    traffic = measured_traffic("k_combine", cfg.name)
+    traffic = measured_traffic("k_combine", traffic_key(cfg, args))
 
     out = {
         "metric": "dispatch+combine HBM GB/s & % of peak, 4096x7168 top-8; us at 128 tokens",
@@ -596,8 +645,10 @@ def main():
         "data": "synthetic (seeded)",
         "config": {"workload": cfg.name, "tokens": cfg.T, "hidden": cfg.H, "experts": cfg.E,
                    "ranks_simulated": cfg.R, "topk": cfg.k, "routing": cfg.routing,
-                   "fp8_dispatch": cfg.use_fp8, "cap_rows": main_path.cap, "kept_slots": N,
-                   "step": ("fused layout+dispatch launch, then combine" if fused
+                   "fp8_dispatch": cfg.use_fp8, "cap_rows": step_buf.cap_rows, "kept_slots": N,
+                   "step": ("low-latency dispatch launch, then combine" if llp is not None else
+                            "rank-deduplicated layout, dispatch, combine (three launches)" if dedp is not None else
+                            "fused layout+dispatch launch, then combine" if fused
                             else "layout, dispatch, combine (three launches)") +
                            ("; eager launches" if args.eager else
                             f"; HIP graph of {per_graph} steps, replayed {K // max(per_graph, 1)} times")},
@@ -610,7 +661,10 @@ def main():
         "eager_step": {"us_per_step": round(eager_ms * 1e3, 2),
                        "GBps": round((d_bytes + c_bytes) / (eager_ms * 1e-3) / 1e9, 1)},
     }
-    if fused:
+    if llp is not None:
+        out["kernels"]["ll_dispatch"] = {"us": round(ld_ms * 1e3, 2), "bytes": d_bytes,
+                                         "GBps": round(d_bytes / (ld_ms * 1e-3) / 1e9, 1)}
+    elif fused:
         out["kernels"]["layout_dispatch"] = {"us": round(ld_ms * 1e3, 2), "bytes": d_bytes,
                                              "GBps": round(d_bytes / (ld_ms * 1e-3) / 1e9, 1)}
     else:
@@ -621,6 +675,12 @@ def main():
     print(f"# main: {ms * 1e3:.1f} us/step  " +
           "  ".join(f"{k} {v['us']:.1f}" for k, v in out["kernels"].items()) + " us", file=sys.stderr, flush=True)
 
+    if llp is not None:
+        llp.buf.close()
+        del llp
+    if dedp is not None:
+        dedp.buf.close()
+        del dedp
     if not args.no_extras:
         # the other form of the same step, on the same buffers
         p = main_path
@@ -652,15 +712,16 @@ def main():
                                                  "GBps": round(c_bytes / (db_ms * 1e-3) / 1e9, 1)},
                            "GBps": round((cb_bytes + c_bytes) / (bms * 1e-3) / 1e9, 1)}
         del grows, gx, gy
-        # plain streaming copy of the combine's byte count (attainable bandwidth)
-        nb = (c_bytes // 2) // 16 * 16
-        src = torch.empty(nb, dtype=torch.uint8, device="cuda")
-        dst = torch.empty(nb, dtype=torch.uint8, device="cuda")
-        src.fill_(1)
-        cms, (copy_ms,) = timed(torch, [lambda: ep.copy_bytes(src, dst)], K, W)
-        out["copy_reference"] = {"bytes_moved": 2 * nb, "us": round(copy_ms * 1e3, 2),
-                                 "GBps": round(2 * nb / (copy_ms * 1e-3) / 1e9, 1)}
-        del src, dst
+    # plain streaming copy of the combine's byte count (attainable
+    # bandwidth; also the counters' calibration in profiled runs)
+    nb = (c_bytes // 2) // 16 * 16
+    src = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    dst = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    cms, (copy_ms,) = timed(torch, [lambda: ep.copy_bytes(src, dst)], K, W)
+    out["copy_reference"] = {"bytes_moved": 2 * nb, "us": round(copy_ms * 1e3, 2),
+                             "GBps": round(2 * nb / (copy_ms * 1e-3) / 1e9, 1)}
+    del src, dst
     if not args.no_extras:
         # rank-deduplicated exchange on the same inputs: one row per
         # (token, destination rank), combine of the pre-reduced rows
