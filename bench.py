@@ -20,6 +20,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -194,6 +195,12 @@ class DedupPath:
         self.buf.dispatch_dedup(m.x, m.topk, m.w, self.layout, m.cfg.use_fp8,
                                 out=(self.recv_x, self.recv_scales, self.recv_topk_idx, self.recv_topk_w,
                                      self.handle))
+
+    def fused_op(self):
+        m = self.main
+        self.buf.dispatch_dedup_with_layout(m.x, m.topk, m.w, m.cfg.use_fp8, layout=self.layout,
+                                            out=(self.recv_x, self.recv_scales, self.recv_topk_idx,
+                                                 self.recv_topk_w, self.handle))
 
     def combine_op(self):
         self.buf.combine(self.expert_out, self.handle, None, out=self.y)
@@ -412,9 +419,11 @@ def measured_traffic(kernel, workload):
 # rocprofv3 summaries -> profiles/
 # ---------------------------------------------------------------------------
 
-KERNELS = {"k_layout": "k_layout<", "k_layout_dispatch": "k_layout_dispatch<", "k_dispatch": "k_dispatch<true, 1>",
-           "k_dispatch_dedup": "k_dispatch<true, 2>", "k_ll_dispatch": "k_ll_dispatch<",
-           "k_combine": "k_combine<false>", "k_copy": "k_copy"}
+KERNELS = {  # regular expressions on the kernel names rocprofv3 reports
+    "k_layout": r"k_layout<", "k_layout_dispatch": r"k_layout_dispatch<\d+, \w+, 1>",
+    "k_layout_dispatch_dedup": r"k_layout_dispatch<\d+, \w+, 2>", "k_dispatch": r"k_dispatch<true, 1>",
+    "k_dispatch_dedup": r"k_dispatch<true, 2>", "k_ll_dispatch": r"k_ll_dispatch<",
+    "k_combine": r"k_combine<false>", "k_copy": r"k_copy"}
 
 
 def _csv_rows(d, suffix):
@@ -434,14 +443,14 @@ def _per_kernel(rows, value_key):
     out = {k: [] for k in KERNELS}
     for r in sorted(rows, key=lambda r: int(r.get("Dispatch_Id", r.get("Correlation_Id", 0)))):
         for k, pat in KERNELS.items():
-            if pat in r["Kernel_Name"]:
+            if re.search(pat, r["Kernel_Name"]):
                 out[k].append((int(r["Grid_Size"]), float(r[value_key])))
     return out
 
 
 def traffic_key(cfg, args):
-    return cfg.name + ("_low_latency" if args.ll else "_dedup" if args.dedup else
-                       "_separate" if args.separate else "")
+    return cfg.name + ("_low_latency" if args.ll else "_dedup" if args.dedup else "") + \
+        ("_separate" if args.separate else "")
 
 
 def mode_flags(args):
@@ -598,14 +607,15 @@ def main():
     if llp is not None:
         main_ops = [llp.dispatch_op, llp.combine_op]
     elif dedp is not None:
-        main_ops = [dedp.layout_op, dedp.dispatch_op, dedp.combine_op]
+        main_ops = [dedp.layout_op, dedp.dispatch_op, dedp.combine_op] if args.separate else \
+            [dedp.fused_op, dedp.combine_op]
     else:
         main_ops = [main_path.fused_op, main_path.combine_op] if fused else \
             [main_path.layout_op, main_path.dispatch_op, main_path.combine_op]
     # eager launches with events around every op: the per-kernel durations
     # (and the step itself with --eager)
     eager_ms, per_op = timed(torch, main_ops, K, W)
-    if fused or llp is not None:
+    if len(per_op) == 2:
         ld_ms, com_ms = per_op
     else:
         lay_ms, dis_ms, com_ms = per_op
@@ -647,7 +657,9 @@ def main():
                    "ranks_simulated": cfg.R, "topk": cfg.k, "routing": cfg.routing,
                    "fp8_dispatch": cfg.use_fp8, "cap_rows": step_buf.cap_rows, "kept_slots": N,
                    "step": ("low-latency dispatch launch, then combine" if llp is not None else
-                            "rank-deduplicated layout, dispatch, combine (three launches)" if dedp is not None else
+                            "rank-deduplicated layout, dispatch, combine (three launches)"
+                            if dedp is not None and args.separate else
+                            "fused rank-deduplicated layout+dispatch launch, then combine" if dedp is not None else
                             "fused layout+dispatch launch, then combine" if fused
                             else "layout, dispatch, combine (three launches)") +
                            ("; eager launches" if args.eager else
@@ -664,7 +676,7 @@ def main():
     if llp is not None:
         out["kernels"]["ll_dispatch"] = {"us": round(ld_ms * 1e3, 2), "bytes": d_bytes,
                                          "GBps": round(d_bytes / (ld_ms * 1e-3) / 1e9, 1)}
-    elif fused:
+    elif len(per_op) == 2:
         out["kernels"]["layout_dispatch"] = {"us": round(ld_ms * 1e3, 2), "bytes": d_bytes,
                                              "GBps": round(d_bytes / (ld_ms * 1e-3) / 1e9, 1)}
     else:
@@ -728,13 +740,19 @@ def main():
         dp = DedupPath(main_path, torch, ep, workloads, args.seed)
         ops = [dp.layout_op, dp.dispatch_op, dp.combine_op]
         e_ms, (l_, d_, c_) = timed(torch, ops, K, W)
-        g_ms, _, _ = graph_step_timed(torch, ops, K, W)
+        g3_ms, _, _ = graph_step_timed(torch, ops, K, W)
+        fops = [dp.fused_op, dp.combine_op]
+        ef_ms, (ld_, _) = timed(torch, fops, K, W)
+        g_ms, _, _ = graph_step_timed(torch, fops, K, W)
         if dp.buf.status():
             raise SystemExit(f"bench: device status {dp.buf.status()} on {cfg.name} (dedup)")
         Nd = dp.rows()
         dd, dc = dedup_bytes(cfg.T, cfg.k, cfg.H, Nd, cfg.use_fp8)
         out["dedup"] = {"workload": cfg.name, "rows": Nd, "rows_per_expert_path": N, "cap_rows": dp.cap,
-                        "us_per_step_graph": round(g_ms * 1e3, 2), "us_per_step_eager": round(e_ms * 1e3, 2),
+                        "us_per_step_graph": round(g_ms * 1e3, 2), "us_per_step_eager": round(ef_ms * 1e3, 2),
+                        "layout_dispatch_us": round(ld_ * 1e3, 2),
+                        "three_calls": {"us_per_step_graph": round(g3_ms * 1e3, 2),
+                                        "us_per_step_eager": round(e_ms * 1e3, 2)},
                         "layout_us": round(l_ * 1e3, 2),
                         "dispatch": {"us": round(d_ * 1e3, 2), "bytes": dd,
                                      "GBps": round(dd / (d_ * 1e-3) / 1e9, 1),
@@ -744,7 +762,8 @@ def main():
                                     "frac": round(dc / (c_ * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
                         "GBps_graph": round((dd + dc) / (g_ms * 1e-3) / 1e9, 1),
                         "speedup_vs_per_expert_step": round(ms / g_ms, 3)}
-        print(f"# dedup: {g_ms * 1e3:.1f} us/step graph, rows {Nd} of {N}", file=sys.stderr, flush=True)
+        print(f"# dedup: {g_ms * 1e3:.1f} us/step graph fused ({g3_ms * 1e3:.1f} three calls), rows {Nd} of {N}",
+              file=sys.stderr, flush=True)
         dp.buf.close()
         del dp
 

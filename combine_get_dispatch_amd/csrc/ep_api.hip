@@ -25,7 +25,7 @@ struct ep_ctx {
     uint32_t spin_limit;
     bool debug;
     int cu_count;
-    int fused_per_cu[2][2];    // [k > 8][fp8]: fused-kernel blocks one CU holds at once (-1: not asked yet)
+    int fused_per_cu[2][2][2];  // [deduplicated][k > 8][fp8]: fused-kernel blocks one CU holds (-1: not asked)
     int cu_budget;             // compute units the caller's stream may use (ep_set_cu_budget; 0 = all)
 };
 
@@ -255,6 +255,20 @@ int fill_layout(ep_ctx *ctx, const int32_t *topk_idx, const ep_layout *L, ep::La
 }
 
 // Shared checks of the forward dispatch arguments; sets the handle's config.
+// The fused layout+dispatch grid, sized for the compute units the caller's
+// stream may use (mode 1: per expert, 2: deduplicated per rank).
+int launch_fused(ep_ctx *ctx, const ep::LayoutArgs &la, const ep::DispatchArgs &da, bool fp8, int mode,
+                 int num_waves, ep_stream_t stream, const char *name) {
+    const ep_config &c = ctx->cfg;
+    int &per_cu = ctx->fused_per_cu[mode == 2][c.num_topk > 8][fp8];
+    if (per_cu < 0)
+        per_cu = ep::layout_dispatch_blocks_per_cu(c.num_topk, fp8, mode,
+                                                   ep::layout_lds_bytes(c.num_experts + c.num_ranks));
+    const int cus = ctx->cu_budget > 0 ? std::min(ctx->cu_budget, ctx->cu_count) : ctx->cu_count;
+    return hip_fail(ep::launch_layout_dispatch(la, da, fp8, mode, num_waves, cus * per_cu, (hipStream_t)stream),
+                    name);
+}
+
 int check_forward_dispatch(ep_ctx *ctx, const int32_t *topk_idx, const float *topk_weights, const ep_layout *L,
                            int use_fp8, float *recv_scales, float *recv_w, ep_handle *handle) {
     if (!ctx || !L || !handle) return EP_ERR_ARG;
@@ -338,7 +352,8 @@ int ep_create(const ep_config *cfg, ep_ctx **out) {
         delete ctx;
         return EP_ERR_HIP;
     }
-    for (auto &row : ctx->fused_per_cu) row[0] = row[1] = -1;
+    for (auto &plane : ctx->fused_per_cu)
+        for (auto &row : plane) row[0] = row[1] = -1;
     ctx->cu_budget = 0;
     if (hipMalloc(&ctx->ws, ctx->ws_bytes) != hipSuccess) {
         delete ctx;
@@ -441,6 +456,30 @@ int ep_dispatch_low_latency(ep_ctx *ctx, const uint16_t *x, const int32_t *topk_
                     "ep_dispatch_low_latency");
 }
 
+int ep_dispatch_dedup_with_layout(ep_ctx *ctx, const uint16_t *x, const int32_t *topk_idx,
+                                  const float *topk_weights, const ep_layout *L, int use_fp8, void *recv_x,
+                                  float *recv_scales, int32_t *recv_topk_idx, float *recv_topk_w, ep_handle *handle,
+                                  ep_stream_t stream) {
+    if (!ctx || !L || !L->token_rows) return EP_ERR_ARG;  // the deduplicated outputs are required
+    ep::LayoutArgs la;
+    if (int r = fill_layout(ctx, topk_idx, L, la)) return r;
+    if (int r = check_forward_dispatch(ctx, topk_idx, topk_weights, L, use_fp8, recv_scales, nullptr, handle))
+        return r;
+    const ep_config &c = ctx->cfg;
+    if (c.num_tokens == 0)  // nothing to pack: the layout alone (zero counts)
+        return hip_fail(ep::launch_layout(la, (hipStream_t)stream), "ep_dispatch_dedup_with_layout");
+    if (!recv_topk_idx && c.cap_rows > 0) return EP_ERR_ARG;
+    if (recv_topk_w && !topk_weights) return EP_ERR_ARG;
+    if (!aligned(recv_topk_idx, 4) || !aligned(recv_topk_w, 4)) return EP_ERR_ALIGN;
+    ep::DispatchArgs da;
+    Geometry g;
+    if (int r = fill_dispatch(ctx, x, topk_idx, topk_weights, L, 2, recv_x, recv_scales, nullptr, handle, da, g))
+        return r;
+    da.recv_topk_idx = recv_topk_idx;
+    da.recv_topk_w = topk_weights ? recv_topk_w : nullptr;
+    return launch_fused(ctx, la, da, use_fp8 != 0, 2, g.num_waves, stream, "ep_dispatch_dedup_with_layout");
+}
+
 int ep_dispatch_with_layout(ep_ctx *ctx, const uint16_t *x, const int32_t *topk_idx, const float *topk_weights,
                             const ep_layout *L, int use_fp8, void *recv_x, float *recv_scales, float *recv_w,
                             ep_handle *handle, ep_stream_t stream) {
@@ -465,12 +504,7 @@ int ep_dispatch_with_layout(ep_ctx *ctx, const uint16_t *x, const int32_t *topk_
     if (ctx->num_tiles == 1 && ep::inblock_lds_bytes(keys, c.num_topk) <= ep::kMaxBlockLds)
         return hip_fail(ep::launch_dispatch_inblock(la, da, use_fp8 != 0, g.num_waves, (hipStream_t)stream),
                         "ep_dispatch_with_layout");
-    int &per_cu = ctx->fused_per_cu[c.num_topk > 8][use_fp8 != 0];
-    if (per_cu < 0)
-        per_cu = ep::layout_dispatch_blocks_per_cu(c.num_topk, use_fp8 != 0, ep::layout_lds_bytes(keys));
-    const int cus = ctx->cu_budget > 0 ? std::min(ctx->cu_budget, ctx->cu_count) : ctx->cu_count;
-    return hip_fail(ep::launch_layout_dispatch(la, da, use_fp8 != 0, g.num_waves, cus * per_cu, (hipStream_t)stream),
-                    "ep_dispatch_with_layout");
+    return launch_fused(ctx, la, da, use_fp8 != 0, 1, g.num_waves, stream, "ep_dispatch_with_layout");
 }
 
 int ep_combine(ep_ctx *ctx, const uint16_t *expert_out, const ep_handle *handle, const float *weights,

@@ -83,10 +83,11 @@ hipError_t launch_dispatch(const DispatchArgs &a, bool fp8, int mode, int num_wa
                            hipStream_t s);
 hipError_t launch_dispatch_inblock(const LayoutArgs &la, const DispatchArgs &da, bool fp8, int num_waves,
                                    hipStream_t s);
+// mode 1 (per expert) or 2 (deduplicated per rank; la.token_rows set);
 // resident_blocks: blocks of the fused kernel the GPU holds at once (0: unknown)
-hipError_t launch_layout_dispatch(const LayoutArgs &la, const DispatchArgs &da, bool fp8, int num_waves,
+hipError_t launch_layout_dispatch(const LayoutArgs &la, const DispatchArgs &da, bool fp8, int mode, int num_waves,
                                   int resident_blocks, hipStream_t s);
-int layout_dispatch_blocks_per_cu(int k, bool fp8, size_t lds);
+int layout_dispatch_blocks_per_cu(int k, bool fp8, int mode, size_t lds);
 hipError_t launch_combine(const CombineArgs &a, bool out_f32, int num_waves, hipStream_t s);
 hipError_t launch_copy(const void *src, void *dst, size_t n16, hipStream_t s);
 hipError_t launch_cu_census(int blocks, int naps, uint32_t *ids, hipStream_t s);

@@ -385,6 +385,92 @@ __device__ __forceinline__ void layout_block(const LayoutArgs &a, int tile, int 
     if (st && replica == 0) atomicOr(&a.counters[kStatus], st);
     __syncthreads();
 
+    const TileView tv{a, masks, agg, excl, K, tile, epoch, single, replica, nrep, t0, ntile,
+                      first_lo, first_hi, publish};
+    const bool dedup = a.token_rows != nullptr;  // deduplicated rows asked for
+
+    // The rank keys: masks (a token is on rank d if one of its kept slots'
+    // experts is; one tile already has them from the ballots), counts and
+    // look-back. Only the per-source counts and the deduplicated rows need
+    // them.
+    auto rank_keys = [&]() {
+        if (!single) {
+            for (int i = tid; i < kTileWaves * a.R; i += kTileTokens) {
+                const int w = i / a.R, d = i - w * a.R;
+                uint64_t m = 0;
+                for (int e = d * a.epr; e < (d + 1) * a.epr; ++e) m |= masks[w * K + e];
+                masks[w * K + a.E + d] = m;
+            }
+            __syncthreads();
+            for (int key = a.E + tid; key < K; key += kTileTokens)
+                tile_counts(masks, wpre, agg, a, K, key, tile, epoch, single);
+        } else if (dedup) {
+            for (int key = a.E + tid; key < K; key += kTileTokens)
+                tile_counts(masks, wpre, agg, a, K, key, tile, epoch, single);
+        }
+        for (int key = a.E + tid; key < K; key += kTileTokens) lookback_key(tv, key);
+    };
+
+    // The deduplicated rows, when asked for (after the rank keys and a
+    // barrier): the leader slot of each of the token's ranks (its first kept
+    // slot there) gets the token's row in that rank, counted like the
+    // per-expert ranks (earlier tiles, earlier waves, earlier lanes of the
+    // rank's token mask); the last tile holds the totals. A fused grid then
+    // raises the tile's flag: deduplicated rows need nothing else.
+    auto dedup_rows = [&]() {
+        if (my_token) {
+            const uint64_t below = bit - 1;
+            uint64_t led = 0;
+            int rr[KMAX];
+#pragma unroll
+            for (int j = 0; j < KMAX; ++j) {
+                rr[j] = -1;
+                if (ev[j] < 0) continue;
+                const int d = rank_of(ev[j], a.epr, a.epr_shift);
+                if ((led >> d) & 1) continue;
+                led |= 1ull << d;
+                const int key = a.E + d;
+                rr[j] = excl[key] + wpre[wave * K + key] + __popcll(masks[wave * K + key] & below);
+            }
+            int32_t *out = a.rank_in_rank + (size_t)t * a.k;
+            if (fused) {
+#pragma unroll
+                for (int j = 0; j < KMAX; ++j)
+                    if (j < a.k) store_agent(out + j, rr[j]);
+            } else if ((a.k & 3) == 0) {
+#pragma unroll
+                for (int j = 0; j < KMAX; j += 4)
+                    if (j < a.k) *reinterpret_cast<int4 *>(out + j) = make_int4(rr[j], rr[j + 1], rr[j + 2], rr[j + 3]);
+            } else {
+#pragma unroll
+                for (int j = 0; j < KMAX; ++j)
+                    if (j < a.k) out[j] = rr[j];
+            }
+        }
+        if (last_tile && replica == 0)
+            for (int d = tid; d < a.R; d += kTileTokens) {
+                const int rows = excl[a.E + d] + agg[a.E + d];
+                a.token_rows[d] = rows;
+                if ((int64_t)rows > a.cap_rows) atomicOr(&a.counters[kStatus], kStCap);
+            }
+        if (fused) {
+            wait_own_stores();
+            __syncthreads();
+            if (tid == 0)
+                __hip_atomic_store(a.rank_ready + (single ? replica : tile), epoch, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        }
+    };
+
+    // A fused grid of deduplicated rows does the rank keys first: its
+    // dispatch waves wait for them alone.
+    const bool rank_first = fused && dedup;
+    if (rank_first) {
+        rank_keys();
+        __syncthreads();
+        dedup_rows();
+    }
+
     // 2. per expert key: tokens in earlier waves and the tile's count;
     //    published at once for the look-back (tile 0's count is already its
     //    inclusive prefix)
@@ -394,8 +480,6 @@ __device__ __forceinline__ void layout_block(const LayoutArgs &a, int tile, int 
     //    wait on them); the rank keys, which only the per-source counts
     //    need, follow the ranks (step 6) so that no thread runs two chains
     //    before the totals.
-    const TileView tv{a, masks, agg, excl, K, tile, epoch, single, replica, nrep, t0, ntile,
-                      first_lo, first_hi, publish};
     for (int key = tid; key < a.E; key += kTileTokens) lookback_key(tv, key);
     __syncthreads();
 
@@ -490,7 +574,8 @@ __device__ __forceinline__ void layout_block(const LayoutArgs &a, int tile, int 
         }
     }
 
-    if (fused) {
+    // (a fused grid of deduplicated rows raised its flags with the rank keys)
+    if (fused && !dedup) {
         // this block's ranks are readable by the dispatch waves from here on
         wait_own_stores();
         __syncthreads();
@@ -499,27 +584,12 @@ __device__ __forceinline__ void layout_block(const LayoutArgs &a, int tile, int 
                                __HIP_MEMORY_SCOPE_AGENT);
     }
 
-    // 6. the rank keys: masks (a token is on rank d if one of its kept slots'
-    //    experts is), counts, look-back; the boundary prefixes of a source that
-    //    ends in a later tile are published once both kinds of keys have
-    //    theirs; the workspace is re-armed once the last tile has seen every
-    //    tile's counts (a tile publishes only after reading the epoch; fused
-    //    grids re-arm when their last block ends)
-    if (!single) {
-        for (int i = tid; i < kTileWaves * a.R; i += kTileTokens) {
-            const int w = i / a.R, d = i - w * a.R;
-            uint64_t m = 0;
-            for (int e = d * a.epr; e < (d + 1) * a.epr; ++e) m |= masks[w * K + e];
-            masks[w * K + a.E + d] = m;
-        }
-        __syncthreads();
-        for (int key = a.E + tid; key < K; key += kTileTokens)
-            tile_counts(masks, wpre, agg, a, K, key, tile, epoch, single);
-    } else if (a.token_rows) {
-        for (int key = a.E + tid; key < K; key += kTileTokens)
-            tile_counts(masks, wpre, agg, a, K, key, tile, epoch, single);
-    }
-    for (int key = a.E + tid; key < K; key += kTileTokens) lookback_key(tv, key);
+    // 6. the rank keys (unless done first, see above), then the boundary
+    //    prefixes of a source that ends in a later tile, published once both
+    //    kinds of keys have theirs; the workspace is re-armed once the last
+    //    tile has seen every tile's counts (a tile publishes only after
+    //    reading the epoch; fused grids re-arm when their last block ends)
+    if (!rank_first) rank_keys();
     if (publish) __threadfence();  // every wave's prefix stores complete before the flag
     __syncthreads();
     if (!single && tid == 0) {
@@ -531,43 +601,7 @@ __device__ __forceinline__ void layout_block(const LayoutArgs &a, int tile, int 
             __hip_atomic_store(&a.counters[kEpoch], ne, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
-    // the deduplicated rows, when asked for: the leader slot of each of the
-    // token's ranks (its first kept slot there) gets the token's row in that
-    // rank, counted like the per-expert ranks (earlier tiles, earlier waves,
-    // earlier lanes of the rank's token mask); the last tile holds the totals
-    if (a.token_rows) {
-        if (my_token) {
-            const uint64_t below = bit - 1;
-            uint64_t led = 0;
-            int rr[KMAX];
-#pragma unroll
-            for (int j = 0; j < KMAX; ++j) {
-                rr[j] = -1;
-                if (ev[j] < 0) continue;
-                const int d = rank_of(ev[j], a.epr, a.epr_shift);
-                if ((led >> d) & 1) continue;
-                led |= 1ull << d;
-                const int key = a.E + d;
-                rr[j] = excl[key] + wpre[wave * K + key] + __popcll(masks[wave * K + key] & below);
-            }
-            int32_t *out = a.rank_in_rank + (size_t)t * a.k;
-            if ((a.k & 3) == 0) {
-#pragma unroll
-                for (int j = 0; j < KMAX; j += 4)
-                    if (j < a.k) *reinterpret_cast<int4 *>(out + j) = make_int4(rr[j], rr[j + 1], rr[j + 2], rr[j + 3]);
-            } else {
-#pragma unroll
-                for (int j = 0; j < KMAX; ++j)
-                    if (j < a.k) out[j] = rr[j];
-            }
-        }
-        if (last_tile && replica == 0)
-            for (int d = tid; d < a.R; d += kTileTokens) {
-                const int rows = excl[a.E + d] + agg[a.E + d];
-                a.token_rows[d] = rows;
-                if ((int64_t)rows > a.cap_rows) atomicOr(&a.counters[kStatus], kStCap);
-            }
-    }
+    if (dedup && !rank_first) dedup_rows();
 
     // 7. per-source counts for the source ranks that end in this tile
     //    (source s = tokens [s*T/R, (s+1)*T/R)); a start boundary owned by an
@@ -650,7 +684,7 @@ __global__ __launch_bounds__(kTileTokens) void k_layout(LayoutArgs a) {
 // What a dispatch wave of a fused launch waits for before reading the layout.
 struct LayoutWait {
     const uint32_t *rank_ready;    // per layout block: epoch once its ranks are written
-    const uint32_t *totals_ready;  // epoch once the expert offsets are written
+    const uint32_t *totals_ready;  // epoch once the expert offsets are written (NULL: not needed)
     uint32_t *status;
     uint32_t epoch, spin_limit;
     int tokens_per_block;          // tokens whose ranks one layout block writes
@@ -664,7 +698,8 @@ __device__ __forceinline__ void wait_for_layout(const LayoutWait &w, int t_first
         const int lo = t_first / w.tokens_per_block, hi = t_last / w.tokens_per_block;
         uint32_t spins = 0;
         for (;;) {
-            bool ready = __hip_atomic_load(w.totals_ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == w.epoch;
+            bool ready = !w.totals_ready ||
+                         __hip_atomic_load(w.totals_ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == w.epoch;
             for (int b = lo; b <= hi && ready; ++b)
                 ready = __hip_atomic_load(w.rank_ready + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == w.epoch;
             if (ready) break;
@@ -692,17 +727,24 @@ __device__ __forceinline__ int slot_row(const DispatchArgs &a, int t, int lane, 
     int p = -1;
     if (MODE == kRowsPerRank) {
         const size_t i = (size_t)t * a.k + lane;
-        int e = -1, kept = 0, d = -1;
+        int e = -1, rr = -1, d = -1;
         float wv = 0.0f;
         if (lane < a.k) {
             e = a.topk[i];
-            kept = a.rank_in_expert[i] >= 0;
             if (a.recv_topk_w) wv = a.w[i];
-            const int rr = a.rank_in_rank[i];
-            if (rr >= 0 && e >= 0 && e < a.E) {
-                d = rank_of(e, a.epr, a.epr_shift);
-                if (rr < a.cap_rows) p = (int)((int64_t)d * a.cap_rows + rr);
-            }
+            rr = FUSED ? __hip_atomic_load(a.rank_in_rank + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                       : a.rank_in_rank[i];
+        }
+        // kept: a valid expert that no earlier slot of the token repeats (the
+        // layout's rule), from the slots themselves
+        int kept = e >= 0 && e < a.E;
+        for (int jj = 0; jj < a.k; ++jj) {
+            const int ej = readlane_i(e, jj);
+            if (jj < lane && ej == e) kept = 0;
+        }
+        if (kept && rr >= 0) {
+            d = rank_of(e, a.epr, a.epr_shift);
+            if (rr < a.cap_rows) p = (int)((int64_t)d * a.cap_rows + rr);
         }
         if (part == 0) {
             if (lane < a.k) {
@@ -1034,7 +1076,7 @@ __global__ __launch_bounds__(kTileTokens) void k_ll_dispatch(DispatchArgs da, in
 // for the layout blocks of their tokens and for the totals, then write the
 // rows. `db` is the block's index among the dispatch blocks, which take the
 // work items [0, items).
-template <bool FP8, int NW>
+template <bool FP8, int NW, int MODE>
 __device__ __forceinline__ void fused_dispatch_block(const DispatchArgs &da, const LayoutWait &lw, int db, int items) {
     const int gw = db * NW + (int)(threadIdx.x >> 6);
     const int t = gw / da.waves_per_token;
@@ -1048,7 +1090,7 @@ __device__ __forceinline__ void fused_dispatch_block(const DispatchArgs &da, con
     const int t_last = min((min(gw0 + NW, items) - 1) / da.waves_per_token, da.T - 1);
     wait_for_layout(lw, t_first, max(t_last, t_first));
     if (active) {
-        const int p = slot_row<kRowsPerExpert, true>(da, t, threadIdx.x & 63, part);
+        const int p = slot_row<MODE, true>(da, t, threadIdx.x & 63, part);
         store_rows<FP8>(da, part, p, v);
     }
 }
@@ -1059,7 +1101,8 @@ __device__ __forceinline__ void wave_wait_for_layout(const LayoutWait &w, int t)
     const uint32_t *flag = w.rank_ready + t / w.tokens_per_block;
     uint32_t spins = 0;
     while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != w.epoch ||
-           __hip_atomic_load(w.totals_ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != w.epoch) {
+           (w.totals_ready &&
+            __hip_atomic_load(w.totals_ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != w.epoch)) {
         if (++spins > w.spin_limit) {
             atomicOr(w.status, kStTimeout);
             break;
@@ -1068,10 +1111,11 @@ __device__ __forceinline__ void wave_wait_for_layout(const LayoutWait &w, int t)
     }
 }
 
-__device__ __forceinline__ LayoutWait make_wait(const LayoutArgs &la, uint32_t epoch, int tokens_per_block) {
+__device__ __forceinline__ LayoutWait make_wait(const LayoutArgs &la, uint32_t epoch, int tokens_per_block,
+                                                bool totals) {
     LayoutWait lw;
     lw.rank_ready = la.rank_ready;
-    lw.totals_ready = la.counters + kTotalsReady;
+    lw.totals_ready = totals ? la.counters + kTotalsReady : nullptr;
     lw.status = la.counters + kStatus;
     lw.epoch = epoch;
     lw.spin_limit = la.spin_limit;
@@ -1103,9 +1147,11 @@ __device__ __forceinline__ void fused_rearm(const LayoutArgs &la) {
 // dispatch block has to wait for a free slot (it would then run its chain of
 // dependent loads behind everyone's row traffic). Not with a ticket: then
 // the layout blocks themselves need the slots their predecessors free.
-template <int KMAX, bool FP8>
+template <int KMAX, bool FP8, int MODE>
 __global__ __launch_bounds__(kTileTokens) void k_layout_dispatch(LayoutArgs la, DispatchArgs da, int lgrid,
                                                                  int extra) {
+    // per expert: ranks and expert offsets (the totals); per rank: leader rows only
+    constexpr bool kTotals = MODE == kRowsPerExpert;
     const int b = (int)blockIdx.x;
     const int items = da.T * da.waves_per_token;
     const int tpb = la.num_tiles > 1 ? kTileTokens : (la.T + lgrid - 1) / lgrid;
@@ -1128,13 +1174,14 @@ __global__ __launch_bounds__(kTileTokens) void k_layout_dispatch(LayoutArgs la, 
             const int part = gw - t * da.waves_per_token;
             u32x4 v[2 * kMaxPassPerWave];
             load_rows<FP8>(da, t, part, true, v);
-            wave_wait_for_layout(make_wait(la, epoch, tpb), t);
-            const int p = slot_row<kRowsPerExpert, true>(da, t, threadIdx.x & 63, part);
+            wave_wait_for_layout(make_wait(la, epoch, tpb, kTotals), t);
+            const int p = slot_row<MODE, true>(da, t, threadIdx.x & 63, part);
             store_rows<FP8>(da, part, p, v);
         }
     } else {
         const uint32_t epoch = load_epoch(la);
-        fused_dispatch_block<FP8, kWavesPerBlock>(da, make_wait(la, epoch, tpb), b - lgrid, items - extra);
+        fused_dispatch_block<FP8, kWavesPerBlock, MODE>(da, make_wait(la, epoch, tpb, kTotals), b - lgrid,
+                                                        items - extra);
     }
     fused_rearm(la);
 }
@@ -1289,19 +1336,37 @@ hipError_t launch_layout(const LayoutArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
-const void *layout_dispatch_fn(int k, bool fp8) {
-    if (k <= 8) return fp8 ? (const void *)k_layout_dispatch<8, true> : (const void *)k_layout_dispatch<8, false>;
-    return fp8 ? (const void *)k_layout_dispatch<kMaxTopk, true> : (const void *)k_layout_dispatch<kMaxTopk, false>;
+template <int KMAX, bool FP8>
+const void *layout_dispatch_kernel(int mode) {
+    return mode == kRowsPerRank ? (const void *)k_layout_dispatch<KMAX, FP8, kRowsPerRank>
+                                : (const void *)k_layout_dispatch<KMAX, FP8, kRowsPerExpert>;
 }
 
-int layout_dispatch_blocks_per_cu(int k, bool fp8, size_t lds) {
+const void *layout_dispatch_fn(int k, bool fp8, int mode) {
+    if (k <= 8) return fp8 ? layout_dispatch_kernel<8, true>(mode) : layout_dispatch_kernel<8, false>(mode);
+    return fp8 ? layout_dispatch_kernel<kMaxTopk, true>(mode) : layout_dispatch_kernel<kMaxTopk, false>(mode);
+}
+
+int layout_dispatch_blocks_per_cu(int k, bool fp8, int mode, size_t lds) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, layout_dispatch_fn(k, fp8), kTileTokens, lds) != hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, layout_dispatch_fn(k, fp8, mode), kTileTokens, lds) !=
+        hipSuccess)
         return 0;
     return n;
 }
 
-hipError_t launch_layout_dispatch(const LayoutArgs &la, const DispatchArgs &da, bool fp8, int num_waves,
+template <int KMAX, bool FP8>
+void launch_layout_dispatch_t(const LayoutArgs &la, const DispatchArgs &da, int mode, dim3 grid, size_t lds,
+                              int lgrid, int extra, hipStream_t s) {
+    if (mode == kRowsPerRank)
+        hipLaunchKernelGGL((k_layout_dispatch<KMAX, FP8, kRowsPerRank>), grid, dim3(kTileTokens), lds, s, la, da,
+                           lgrid, extra);
+    else
+        hipLaunchKernelGGL((k_layout_dispatch<KMAX, FP8, kRowsPerExpert>), grid, dim3(kTileTokens), lds, s, la, da,
+                           lgrid, extra);
+}
+
+hipError_t launch_layout_dispatch(const LayoutArgs &la, const DispatchArgs &da, bool fp8, int mode, int num_waves,
                                   int resident_blocks, hipStream_t s) {
     const size_t lds = layout_lds_bytes(la.E + la.R);
     const int lgrid = la.num_tiles > 1 ? la.num_tiles : max(1, min(la.R, kLayoutReplicas));
@@ -1311,18 +1376,17 @@ hipError_t launch_layout_dispatch(const LayoutArgs &la, const DispatchArgs &da, 
     const int full = lgrid + (num_waves + kWavesPerBlock - 1) / kWavesPerBlock;
     if (!la.use_ticket && resident_blocks > 0 && full > resident_blocks)
         extra = min(num_waves, min(lgrid, full - resident_blocks) * kWavesPerBlock);
-    const int grid = lgrid + (num_waves - extra + kWavesPerBlock - 1) / kWavesPerBlock;
-    const dim3 block(kTileTokens);
+    const dim3 grid(lgrid + (num_waves - extra + kWavesPerBlock - 1) / kWavesPerBlock);
     if (la.k <= 8) {
         if (fp8)
-            hipLaunchKernelGGL((k_layout_dispatch<8, true>), dim3(grid), block, lds, s, la, da, lgrid, extra);
+            launch_layout_dispatch_t<8, true>(la, da, mode, grid, lds, lgrid, extra, s);
         else
-            hipLaunchKernelGGL((k_layout_dispatch<8, false>), dim3(grid), block, lds, s, la, da, lgrid, extra);
+            launch_layout_dispatch_t<8, false>(la, da, mode, grid, lds, lgrid, extra, s);
     } else {
         if (fp8)
-            hipLaunchKernelGGL((k_layout_dispatch<kMaxTopk, true>), dim3(grid), block, lds, s, la, da, lgrid, extra);
+            launch_layout_dispatch_t<kMaxTopk, true>(la, da, mode, grid, lds, lgrid, extra, s);
         else
-            hipLaunchKernelGGL((k_layout_dispatch<kMaxTopk, false>), dim3(grid), block, lds, s, la, da, lgrid, extra);
+            launch_layout_dispatch_t<kMaxTopk, false>(la, da, mode, grid, lds, lgrid, extra, s);
     }
     return hipGetLastError();
 }

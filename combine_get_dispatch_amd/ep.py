@@ -78,6 +78,9 @@ SIGNATURES = {
     "ep_dispatch_dedup": (ctypes.c_int, [c_void_p, c_void_p, c_void_p, c_void_p, ctypes.POINTER(EpLayout),
                                          ctypes.c_int, c_void_p, c_void_p, c_void_p, c_void_p,
                                          ctypes.POINTER(EpHandle), c_void_p]),
+    "ep_dispatch_dedup_with_layout": (ctypes.c_int, [c_void_p, c_void_p, c_void_p, c_void_p,
+                                                     ctypes.POINTER(EpLayout), ctypes.c_int, c_void_p, c_void_p,
+                                                     c_void_p, c_void_p, ctypes.POINTER(EpHandle), c_void_p]),
     "ep_dispatch_low_latency": (ctypes.c_int, [c_void_p, c_void_p, c_void_p, c_void_p, ctypes.c_int, c_void_p,
                                                c_void_p, c_void_p, c_void_p, ctypes.POINTER(EpHandle),
                                                c_void_p]),
@@ -183,6 +186,15 @@ def ep_dispatch_dedup(ctx: int, x: int, topk_idx: int, topk_weights: Optional[in
     _check(load().ep_dispatch_dedup(ctx, x, topk_idx, topk_weights, ctypes.byref(layout), int(use_fp8),
                                     recv_x, recv_scales, recv_topk_idx, recv_topk_w, ctypes.byref(handle),
                                     stream), "ep_dispatch_dedup")
+
+
+def ep_dispatch_dedup_with_layout(ctx: int, x: int, topk_idx: int, topk_weights: Optional[int],
+                                  layout: EpLayout, use_fp8: int, recv_x: int, recv_scales: Optional[int],
+                                  recv_topk_idx: Optional[int], recv_topk_w: Optional[int], handle: EpHandle,
+                                  stream: int) -> None:
+    _check(load().ep_dispatch_dedup_with_layout(ctx, x, topk_idx, topk_weights, ctypes.byref(layout),
+                                                int(use_fp8), recv_x, recv_scales, recv_topk_idx, recv_topk_w,
+                                                ctypes.byref(handle), stream), "ep_dispatch_dedup_with_layout")
 
 
 def ep_dispatch_low_latency(ctx: int, x: int, topk_idx: int, topk_weights: Optional[int], use_fp8: int,
@@ -442,6 +454,27 @@ class Buffer:
                           _ptr(recv_topk_w), ch, _stream())
         handle.num_tokens, handle.num_topk = ch.num_tokens, ch.num_topk
         return recv_x, recv_scales, recv_topk_idx, recv_topk_w, handle
+
+    def dispatch_dedup_with_layout(self, x, topk_idx, topk_weights, use_fp8: bool, layout: Optional[Layout] = None,
+                                   out=None):
+        """Deduplicated layout and dispatch in one launch. Returns (layout,
+        recv_x, recv_scales, recv_topk_idx, recv_topk_w, handle)."""
+        t = self.torch
+        layout = layout or self.new_layout(dedup=True)
+        if out is None:
+            recv_x = self._empty((self.num_rows, self.H), t.uint8 if use_fp8 else t.bfloat16)
+            recv_scales = self._empty((self.num_rows, self.H // 128), t.float32) if use_fp8 else None
+            recv_topk_idx = self._empty((self.num_rows, self.k), t.int32)
+            recv_topk_w = self._empty((self.num_rows, self.k), t.float32) if topk_weights is not None else None
+            handle = self.new_handle()
+        else:
+            recv_x, recv_scales, recv_topk_idx, recv_topk_w, handle = out
+        ch = handle.c()
+        ep_dispatch_dedup_with_layout(self.ctx, x.data_ptr(), topk_idx.data_ptr(), _ptr(topk_weights), layout.c(),
+                                      int(bool(use_fp8)), recv_x.data_ptr(), _ptr(recv_scales),
+                                      _ptr(recv_topk_idx), _ptr(recv_topk_w), ch, _stream())
+        handle.num_tokens, handle.num_topk = ch.num_tokens, ch.num_topk
+        return layout, recv_x, recv_scales, recv_topk_idx, recv_topk_w, handle
 
     def dispatch_low_latency(self, x, topk_idx, topk_weights, use_fp8: bool, out=None):
         """Low-latency dispatch (the buffer must have cap_rows =

@@ -213,6 +213,18 @@ int ep_dispatch_dedup(ep_ctx *ctx, const uint16_t *x, const int32_t *topk_idx,
                       void *recv_x, float *recv_scales, int32_t *recv_topk_idx, float *recv_topk_w,
                       ep_handle *handle, ep_stream_t stream);
 
+/* ep_get_dispatch_layout (with rank_in_rank and token_rows, which are
+ * required here) followed by ep_dispatch_dedup, in one launch: the same
+ * outputs bit for bit. The layout blocks raise a flag once a tile's leader
+ * rows are written and the dispatch waves, which have already loaded their
+ * rows of x, wait on it only to place them (no wait for the expert totals:
+ * deduplicated rows do not use them). Same arguments and requirements as the
+ * two calls it replaces; calls on one context are ordered by the stream. */
+int ep_dispatch_dedup_with_layout(ep_ctx *ctx, const uint16_t *x, const int32_t *topk_idx,
+                                  const float *topk_weights, const ep_layout *layout, int use_fp8,
+                                  void *recv_x, float *recv_scales, int32_t *recv_topk_idx,
+                                  float *recv_topk_w, ep_handle *handle, ep_stream_t stream);
+
 /* Low-latency dispatch (the low-latency kernels of the DeepEP notes, section
  * 1: decode batches, a receive buffer fixed in advance, no count exchange;
  * section 5: at most 256 tokens per rank). One launch, no layout call, no

@@ -4,6 +4,7 @@ C ABI: the layout's leader ranks and per-rank token counts, the handle, the
 received rows (bf16 copies or e4m3 codes + scales), each row's routing
 entries, and the combine of pre-reduced rows. Integer, index and byte outputs
 bit-exact; the bf16 combine bit-exact (same fp32 FMA order as the oracle)."""
+import gc
 from dataclasses import replace
 
 import numpy as np
@@ -12,7 +13,7 @@ import torch
 
 import oracle
 from combine_get_dispatch_amd import ep
-from combine_get_dispatch_amd.workloads import CONFIGS, make_workload, normal_bf16, to_bf16_bits
+from combine_get_dispatch_amd.workloads import CONFIGS, device_normal_bf16, make_workload, normal_bf16, to_bf16_bits
 from gpu_helpers import LAYOUT_KEYS, compare_bf16, dev, dev_bf16, host, host_u16, used_rows
 
 pytestmark = pytest.mark.gpu
@@ -27,19 +28,23 @@ def dedup_cap(topk, E, R):
     return int(rows.max()) if rows.size else 0
 
 
-def gpu_dedup(x, topk, w, E, R, cap, fp8):
+def gpu_dedup(x, topk, w, E, R, cap, fp8, fused=False):
+    """Layout + deduplicated dispatch: two calls, or the fused one."""
     T, k = topk.shape
     H = x.shape[1]
     buf = ep.Buffer(T, H, k, E, R, cap)
     topk_d = dev(topk.astype(np.int32))
     w_d = None if w is None else dev(w.astype(np.float32))
-    L = buf.get_dispatch_layout(topk_d, buf.new_layout(dedup=True))
-    rx, rs, rti, rtw, h = buf.dispatch_dedup(dev_bf16(x), topk_d, w_d, L, fp8)
+    if fused:
+        L, rx, rs, rti, rtw, h = buf.dispatch_dedup_with_layout(dev_bf16(x), topk_d, w_d, fp8)
+    else:
+        L = buf.get_dispatch_layout(topk_d, buf.new_layout(dedup=True))
+        rx, rs, rti, rtw, h = buf.dispatch_dedup(dev_bf16(x), topk_d, w_d, L, fp8)
     st = buf.status()
     return buf, L, rx, rs, rti, rtw, h, st
 
 
-def check_dedup(x, topk, w, E, R, cap, fp8, combine_seed=7):
+def check_dedup(x, topk, w, E, R, cap, fp8, combine_seed=7, fused=False):
     """Layout, handle, rows, routing entries and combine, every element."""
     orc = oracle.default()
     T, k = topk.shape
@@ -49,7 +54,7 @@ def check_dedup(x, topk, w, E, R, cap, fp8, combine_seed=7):
     n = R * cap
     rx_o, rs_o, rti_o, rtw_o = orc.dispatch_dedup(x, topk, w, pos_o, E, R, n, fp8)
 
-    buf, L, rx, rs, rti, rtw, h, st = gpu_dedup(x, topk, w, E, R, cap, fp8)
+    buf, L, rx, rs, rti, rtw, h, st = gpu_dedup(x, topk, w, E, R, cap, fp8, fused)
     assert st == st_o, (st, st_o)
     for key in LAYOUT_KEYS:  # the per-expert layout is unchanged
         assert np.array_equal(host(getattr(L, key)), getattr(Lo, key)), key
@@ -86,12 +91,13 @@ def check_dedup(x, topk, w, E, R, cap, fp8, combine_seed=7):
     return st_o, pos_o, trows_o
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["two_calls", "fused"])
 @pytest.mark.parametrize("name", ["tiny", "decode_rank", "decode", "prefill", "skewed"])
-def test_dedup_parity(name):
+def test_dedup_parity(name, fused):
     cfg = CONFIGS[name]
     wl = make_workload(cfg, seed=0)
     cap = dedup_cap(wl.topk_idx, cfg.E, cfg.R)
-    st, pos, trows = check_dedup(wl.x, wl.topk_idx, wl.topk_w, cfg.E, cfg.R, cap, cfg.use_fp8)
+    st, pos, trows = check_dedup(wl.x, wl.topk_idx, wl.topk_w, cfg.E, cfg.R, cap, cfg.use_fp8, fused=fused)
     assert st == 0
     # a token lands once per rank it has experts on: fewer rows than slots
     # whenever some token has two experts on one rank
@@ -106,7 +112,7 @@ def test_dedup_bf16_and_fp8_same_routing():
         check_dedup(wl.x, wl.topk_idx, wl.topk_w, cfg.E, cfg.R, cap, fp8)
 
 
-def rand_case(T, k, E, R, H, fp8, seed=0, mutate=None, cap=None, cap_delta=0, weights=True):
+def rand_case(T, k, E, R, H, fp8, seed=0, mutate=None, cap=None, cap_delta=0, weights=True, fused=False):
     rng = np.random.default_rng(seed)
     topk = (np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32) if T > 0
             else np.zeros((0, k), np.int32))
@@ -116,7 +122,7 @@ def rand_case(T, k, E, R, H, fp8, seed=0, mutate=None, cap=None, cap_delta=0, we
     x = to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
     if cap is None:
         cap = max(dedup_cap(topk, E, R) + cap_delta, 0)
-    return check_dedup(x, topk, w, E, R, cap, fp8)
+    return check_dedup(x, topk, w, E, R, cap, fp8, fused=fused)
 
 
 DEDUP_EDGE = {
@@ -138,9 +144,10 @@ DEDUP_EDGE = {
 }
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["two_calls", "fused"])
 @pytest.mark.parametrize("name", list(DEDUP_EDGE))
-def test_dedup_edges(name):
-    rand_case(**DEDUP_EDGE[name])
+def test_dedup_edges(name, fused):
+    rand_case(**DEDUP_EDGE[name], fused=fused)
 
 
 def test_dedup_bad_repeated_and_empty_slots():
@@ -152,13 +159,15 @@ def test_dedup_bad_repeated_and_empty_slots():
         t[5, 2] = t[5, 0] = 1   # repeat
         t[6, :] = 2             # all repeats: one row
         return t
-    st, *_ = rand_case(T=640, k=8, E=64, R=8, H=256, fp8=True, mutate=m)
-    assert st == ep.EP_ST_BAD_EXPERT | ep.EP_ST_DUP_EXPERT
+    for fused in (False, True):
+        st, *_ = rand_case(T=640, k=8, E=64, R=8, H=256, fp8=True, mutate=m, fused=fused)
+        assert st == ep.EP_ST_BAD_EXPERT | ep.EP_ST_DUP_EXPERT
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["two_calls", "fused"])
 @pytest.mark.parametrize("T", [1024, 200])  # several tiles; one tile
-def test_dedup_capacity_drops_rows(T):
-    st, pos, trows = rand_case(T=T, k=8, E=64, R=8, H=512, fp8=True, cap_delta=-5)
+def test_dedup_capacity_drops_rows(T, fused):
+    st, pos, trows = rand_case(T=T, k=8, E=64, R=8, H=512, fp8=True, cap_delta=-5, fused=fused)
     assert st == ep.EP_ST_CAPACITY and 0 < (pos >= 0).sum() < trows.sum()
 
 
@@ -236,3 +245,46 @@ def test_dedup_and_per_expert_interleaved():
             for key in LAYOUT_KEYS:
                 assert np.array_equal(host(getattr(Lp, key)), getattr(Lo, key)), key
         assert buf.status() == 0
+
+
+@pytest.mark.parametrize("name", ["decode_rank", "decode"])  # one tile (replicas); four tiles
+def test_dedup_fused_graph_replay_and_interleaving(name):
+    """The fused deduplicated call captured in a HIP graph with a combine,
+    replayed with per-expert fused calls and layouts in between on the same
+    context (shared flags and epochs): every replay equals the eager result."""
+    cfg = CONFIGS[name]
+    wl = make_workload(cfg, seed=2)
+    cap = int(oracle.default().layout(wl.topk_idx, cfg.E, cfg.R, 1 << 30).rank_rows.max())
+    buf = ep.Buffer(cfg.T, cfg.H, cfg.k, cfg.E, cfg.R, cap)
+    x, topk, w = dev_bf16(wl.x), dev(wl.topk_idx), dev(wl.topk_w)
+    L = buf.new_layout(dedup=True)
+    out = buf.dispatch_dedup_with_layout(x, topk, w, True, layout=L)[1:]
+    out[2].fill_(-3)  # rows no token uses keep this
+    buf.dispatch_dedup_with_layout(x, topk, w, True, layout=L, out=out)
+    eo = device_normal_bf16((buf.num_rows, cfg.H), seed=6)
+    y = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device="cuda")
+    buf.combine(eo, out[4], None, out=y)
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (L.rank_in_rank, L.token_rows, out[4].pos, out[2], y)]
+    gc.collect()  # no buffer of an earlier test may be released during the capture
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g):
+            buf.dispatch_dedup_with_layout(x, topk, w, True, layout=L, out=out)
+            buf.combine(eo, out[4], None, out=y)
+    torch.cuda.current_stream().wait_stream(side)
+    for i in range(4):
+        for t in (L.rank_in_rank, out[4].pos, out[2], y):
+            t.fill_(-3) if t.dtype == torch.int32 else t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [L.rank_in_rank, L.token_rows, out[4].pos, out[2], y]
+        assert all(torch.equal(a, b) for a, b in zip(got, ref)), f"replay {i}"
+        # per-expert work on the same context between replays
+        buf.dispatch_with_layout(x, topk, w, True)
+        buf.get_dispatch_layout(topk)
+    assert buf.status() == 0
