@@ -767,6 +767,26 @@ def main():
         dp.buf.close()
         del dp
 
+    if not args.no_extras and cfg.T // cfg.R <= 256:
+        # the low-latency form at this shape: same rows and bytes, fixed
+        # per-(expert, source) regions, no look-back
+        lp = LlPath(main_path, torch, ep, workloads, args.seed)
+        ops = [lp.dispatch_op, lp.combine_op]
+        le_ms, (lld_, llc_) = timed(torch, ops, K, W)
+        lg_ms, _, _ = graph_step_timed(torch, ops, K, W)
+        if lp.buf.status():
+            raise SystemExit(f"bench: device status {lp.buf.status()} on {cfg.name} (low latency)")
+        out["low_latency"] = {"workload": cfg.name, "us_per_step_graph": round(lg_ms * 1e3, 2),
+                              "GBps_graph": round((d_bytes + c_bytes) / (lg_ms * 1e-3) / 1e9, 1),
+                              "us_per_step_eager": round(le_ms * 1e3, 2),
+                              "dispatch": {"us": round(lld_ * 1e3, 2),
+                                           "GBps": round(d_bytes / (lld_ * 1e-3) / 1e9, 1)},
+                              "combine_us": round(llc_ * 1e3, 2),
+                              "receive_rows": lp.buf.num_rows}
+        print(f"# low latency at {cfg.name}: {lg_ms * 1e3:.1f} us/step graph", file=sys.stderr, flush=True)
+        lp.buf.close()
+        del lp
+
     if not args.no_extras:
         out["cu_cap_overlap"] = cu_cap_overlap(torch, ep, main_path, K, W)
         print("# overlap: " + json.dumps(out["cu_cap_overlap"]), file=sys.stderr, flush=True)
