@@ -592,7 +592,8 @@ def main():
             c_b = dc_b
         res, trace = record_traffic(args, cfg, (c_b // 2) // 16 * 16)  # the copy the bench ran
         write_profile_summaries(args, cfg, res, trace, {"k_layout_dispatch": d_b, "k_dispatch": d_b, "k_combine": c_b,
-                                                        "k_ll_dispatch": d_b, "k_dispatch_dedup": dd_b})
+                                                        "k_ll_dispatch": d_b, "k_dispatch_dedup": dd_b,
+                                                        "k_layout_dispatch_dedup": dd_b})
         print(json.dumps(res))
         return
 
