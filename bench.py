@@ -48,6 +48,9 @@ def parse():
     p.add_argument("--separate", action="store_true",
                    help="time the step as three calls (layout, dispatch, combine) instead of the fused "
                         "layout+dispatch launch followed by combine")
+    p.add_argument("--tokens-per-rank", action="store_true",
+                   help="read the workload's token count as per source rank (T x R tokens on the GPU) "
+                        "instead of per GPU")
     p.add_argument("--ll", action="store_true",
                    help="time the low-latency form as the step (one dispatch launch into fixed "
                         "per-(expert, source) regions, then combine); implies --no-extras")
@@ -575,6 +578,10 @@ def main():
         sys.exit(2)
     from combine_get_dispatch_amd import workloads
     cfg = workloads.CONFIGS[args.config]
+    if args.tokens_per_rank:
+        # the other reading of "N tokens": N on every source rank, R*N on the GPU
+        from dataclasses import replace
+        cfg = replace(cfg, T=cfg.T * cfg.R)
     K, W = args.steps, args.warmup
     if args.record_traffic:
         # no GPU work: summarize the profiler output of an earlier run of this bench
@@ -654,7 +661,9 @@ def main():
         "vs_baseline": None,
         "dtype": "fp8-e4m3 dispatch / bf16 rows / fp32 accumulate" if cfg.use_fp8 else "bf16 / fp32 accumulate",
         "data": "synthetic (seeded)",
-        "config": {"workload": cfg.name, "tokens": cfg.T, "hidden": cfg.H, "experts": cfg.E,
+        "config": {"workload": cfg.name, "tokens": cfg.T,
+                   "tokens_read_as": "per source rank" if args.tokens_per_rank else "per GPU",
+                   "hidden": cfg.H, "experts": cfg.E,
                    "ranks_simulated": cfg.R, "topk": cfg.k, "routing": cfg.routing,
                    "fp8_dispatch": cfg.use_fp8, "cap_rows": step_buf.cap_rows, "kept_slots": N,
                    "step": ("low-latency dispatch launch, then combine" if llp is not None else
