@@ -182,12 +182,13 @@ int ep_dispatch(ep_ctx *ctx, const uint16_t *x, const int32_t *topk_idx,
 /* ep_get_dispatch_layout followed by ep_dispatch, in one launch: the same
  * outputs (layout, handle, received rows, scales and weights), bit for bit.
  * Up to 256 tokens every dispatch block computes the whole layout in its own
- * LDS (no block waits on another); beyond that the layout blocks raise flags
- * in the workspace and the dispatch waves, which have already loaded their
- * rows of x, wait on them only to place the rows. Same arguments and
- * requirements as the two calls it replaces (a layout with rank_in_rank or
- * token_rows set: EP_ERR_ARG); calls on one context are ordered by the
- * stream (two streams sharing a context race). */
+ * LDS (no block waits on another); up to 4096 tokens the layout blocks raise
+ * flags in the workspace and the dispatch waves, which have already loaded
+ * their rows of x, wait on them only to place the rows; beyond 4096 tokens
+ * the call makes the two launches it replaces (faster there). Same
+ * arguments and requirements as the two calls it replaces (a layout with
+ * rank_in_rank or token_rows set: EP_ERR_ARG); calls on one context are
+ * ordered by the stream (two streams sharing a context race). */
 int ep_dispatch_with_layout(ep_ctx *ctx, const uint16_t *x, const int32_t *topk_idx,
                             const float *topk_weights, const ep_layout *layout, int use_fp8,
                             void *recv_x, float *recv_scales, float *recv_w, ep_handle *handle,
@@ -218,8 +219,9 @@ int ep_dispatch_dedup(ep_ctx *ctx, const uint16_t *x, const int32_t *topk_idx,
  * outputs bit for bit. The layout blocks raise a flag once a tile's leader
  * rows are written and the dispatch waves, which have already loaded their
  * rows of x, wait on it only to place them (no wait for the expert totals:
- * deduplicated rows do not use them). Same arguments and requirements as the
- * two calls it replaces; calls on one context are ordered by the stream. */
+ * deduplicated rows do not use them). Beyond 4096 tokens, two launches.
+ * Same arguments and requirements as the two calls it replaces; calls on
+ * one context are ordered by the stream. */
 int ep_dispatch_dedup_with_layout(ep_ctx *ctx, const uint16_t *x, const int32_t *topk_idx,
                                   const float *topk_weights, const ep_layout *layout, int use_fp8,
                                   void *recv_x, float *recv_scales, int32_t *recv_topk_idx,
