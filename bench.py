@@ -424,8 +424,8 @@ def measured_traffic(kernel, workload):
 
 KERNELS = {  # regular expressions on the kernel names rocprofv3 reports
     "k_layout": r"k_layout<", "k_layout_dispatch": r"k_layout_dispatch<\d+, \w+, 1>",
-    "k_layout_dispatch_dedup": r"k_layout_dispatch<\d+, \w+, 2>", "k_dispatch": r"k_dispatch<true, 1>",
-    "k_dispatch_dedup": r"k_dispatch<true, 2>", "k_ll_dispatch": r"k_ll_dispatch<",
+    "k_layout_dispatch_dedup": r"k_layout_dispatch<\d+, \w+, 2>", "k_dispatch": r"k_dispatch<true, 1(, \w+)?>",
+    "k_dispatch_dedup": r"k_dispatch<true, 2(, \w+)?>", "k_ll_dispatch": r"k_ll_dispatch<",
     "k_combine": r"k_combine<false>", "k_copy": r"k_copy"}
 
 
