@@ -139,3 +139,12 @@ def test_cu_mask_rejects(lib, bad):
 def test_low_latency_rejects_other_receive_sizes(lib):
     assert lib.ep_dispatch_low_latency(None, None, None, None, 0, None, None, None, None, None, None) == ep.EP_ERR_ARG
     assert ep.ll_cap_rows(1024, 256, 8) == 32768  # every expert holds T rows: R*cap_rows = E*T
+
+
+def test_new_entry_points_reject_null_without_gpu(lib):
+    L = lib
+    assert L.ep_dispatch_dedup_with_layout(None, None, None, None, None, 0, None, None, None, None, None,
+                                           None) == ep.EP_ERR_ARG
+    assert L.ep_set_cu_budget(None, 8) == ep.EP_ERR_ARG
+    assert L.ep_cu_census(0, 0, None, None) == ep.EP_OK  # nothing to launch
+    assert L.ep_cu_census(16, 65, None, None) == ep.EP_ERR_ARG
