@@ -310,9 +310,10 @@ def cu_cap_overlap(torch, ep, p, K, W):
     return res
 
 
-def timed(torch, ops, K, W):
+def timed(torch, ops, K, W, stats=None):
     """W untimed warmups, then exactly K steps between synchronizations; HIP
-    events (torch's current stream = the launch stream) bracket every op."""
+    events (torch's current stream = the launch stream) bracket every op
+    (their p10 / median / p90 go to `stats` when given)."""
     for _ in range(W):
         for op in ops:
             op()
@@ -327,6 +328,10 @@ def timed(torch, ops, K, W):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     per_op = [sum(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(K)) / K for j in range(len(ops))]
+    if stats is not None:  # p10 / median / p90 of every op, in ms
+        for j in range(len(ops)):
+            xs = sorted(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(K))
+            stats.append(tuple(xs[min(K - 1, int(q * K))] for q in (0.1, 0.5, 0.9)))
     return wall / K * 1e3, per_op  # ms per step, ms per op
 
 
@@ -533,10 +538,22 @@ def write_profile_summaries(args, cfg, res, trace, algo):
         f.write("\n".join(lines) + "\n")
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(path, seconds):
     """The oracle as it stands (single-threaded C) on the same workload:
     layout + positions + FP8 dispatch + combine, repeated whole steps until
-    about `seconds` of CPU time have elapsed."""
+    about `seconds` of CPU time have elapsed, pinned to one core; each op is
+    timed on its own as well (median over the steps)."""
     import numpy as np
     import oracle
     cfg = path.cfg
@@ -545,25 +562,42 @@ def cpu_baseline(path, seconds):
     cap = path.cap
     n = cfg.R * cap
     eo = path.expert_out.view(path.torch.int16).cpu().numpy().view(np.uint16)
+    try:
+        old_aff = os.sched_getaffinity(0)
+        os.sched_setaffinity(0, {sorted(old_aff)[min(1, len(old_aff) - 1)]})
+    except (AttributeError, OSError):
+        old_aff = None
     steps = 0
+    ops = {"layout": [], "positions": [], "dispatch": [], "combine": []}
     t0 = time.perf_counter()
     nk = 0
     while True:
+        a = time.perf_counter()
         L = orc.layout(wl.topk_idx, cfg.E, cfg.R, cap)
+        b = time.perf_counter()
         pos, _ = orc.positions(wl.topk_idx, L, cfg.E, cfg.R, cap)
+        c_ = time.perf_counter()
         orc.dispatch(wl.x, wl.topk_w, pos, n, cfg.use_fp8)
+        d_ = time.perf_counter()
         orc.combine(eo, pos, wl.topk_w)
+        e_ = time.perf_counter()
+        for name, dt in zip(ops, (b - a, c_ - b, d_ - c_, e_ - d_)):
+            ops[name].append(dt)
         nk = int((pos >= 0).sum())
         steps += 1
         el = time.perf_counter() - t0
         if el >= seconds or steps >= 50:
             break
+    if old_aff is not None:
+        os.sched_setaffinity(0, old_aff)
     d, c, _ = algo_bytes(cfg.T, cfg.k, cfg.H, nk, cfg.use_fp8)
     per_step = el / steps
     return {"value": round((d + c) / per_step / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{steps} whole {cfg.name} steps (layout+positions+dispatch+combine, "
-                      f"T={cfg.T}), {per_step * 1e3:.1f} ms/step, single-threaded C oracle",
-            "ms_per_step": round(per_step * 1e3, 2)}
+                      f"T={cfg.T}), {per_step * 1e3:.1f} ms/step, single-threaded C oracle on one pinned core",
+            "ms_per_step": round(per_step * 1e3, 2),
+            "median_ms": {k: round(sorted(v)[len(v) // 2] * 1e3, 2) for k, v in ops.items()},
+            "host": {"cpu": cpu_model(), "nproc": os.cpu_count()}}
 
 
 def main():
@@ -622,7 +656,8 @@ def main():
             [main_path.layout_op, main_path.dispatch_op, main_path.combine_op]
     # eager launches with events around every op: the per-kernel durations
     # (and the step itself with --eager)
-    eager_ms, per_op = timed(torch, main_ops, K, W)
+    op_stats = []
+    eager_ms, per_op = timed(torch, main_ops, K, W, op_stats)
     if len(per_op) == 2:
         ld_ms, com_ms = per_op
     else:
@@ -701,6 +736,30 @@ def main():
         out["kernels"]["dispatch"] = {"us": round(dis_ms * 1e3, 2), "bytes": d_bytes,
                                       "GBps": round(d_bytes / (dis_ms * 1e-3) / 1e9, 1)}
     out["kernels"]["combine"] = {"us": round(com_ms * 1e3, 2), "bytes": c_bytes, "GBps": round(achieved, 1)}
+    for kname, (p10, p50, p90) in zip(out["kernels"], op_stats):
+        out["kernels"][kname].update({"p10_us": round(p10 * 1e3, 2), "median_us": round(p50 * 1e3, 2),
+                                      "p90_us": round(p90 * 1e3, 2)})
+    if not args.no_extras:
+        # the same eager steps, each after a 1 GiB write that evicts the
+        # 256 MB memory-side cache (outside the events)
+        scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        fl = []
+        for i in range(W + K):
+            scratch.fill_(i & 255)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for op in main_ops:
+                op()
+            e1.record()
+            if i >= W:
+                fl.append((e0, e1))
+        torch.cuda.synchronize()
+        fl_ms = sorted(a.elapsed_time(b) for a, b in fl)
+        out["eager_step_after_mall_flush"] = {"median_us": round(fl_ms[K // 2] * 1e3, 2),
+                                              "mean_us": round(sum(fl_ms) / K * 1e3, 2),
+                                              "GBps_median": round((d_bytes + c_bytes) / (fl_ms[K // 2] * 1e-3) / 1e9,
+                                                                   1)}
+        del scratch
     print(f"# main: {ms * 1e3:.1f} us/step  " +
           "  ".join(f"{k} {v['us']:.1f}" for k, v in out["kernels"].items()) + " us", file=sys.stderr, flush=True)
 
