@@ -1,0 +1,61 @@
+"""The bounded waits: a context created with a spin limit of 1 (EP_SPIN_LIMIT,
+read by ep_create) makes the fused launch's waits give up at once, which
+the status word must report as EP_ST_TIMEOUT; the launch still ends and
+writes only inside its buffers (positions are bounds-checked), and a fresh
+context computes the layout and positions exactly. The condition is forced
+from the host; no kernel is made to hang."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from combine_get_dispatch_amd import ep
+from combine_get_dispatch_amd.workloads import to_bf16_bits
+from gpu_helpers import dev, dev_bf16, host
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    ep.load()  # the HIP library must be the path that runs; no fallback
+
+
+@pytest.mark.parametrize("dedup", [False, True], ids=["per_expert", "dedup"])
+def test_spin_limit_reports_timeout_then_fresh_context_is_exact(monkeypatch, dedup):
+    T, k, E, R, H = 4096, 8, 256, 32, 256  # sixteen tiles: the fused launch with flags
+    rng = np.random.default_rng(9)
+    topk = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32)
+    w = rng.random((T, k)).astype(np.float32)
+    x = dev_bf16(to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32)))
+    orc = oracle.default()
+    L_o = orc.layout(topk, E, R, 1 << 30)
+    cap = int(L_o.rank_rows.max())
+    td, wd = dev(topk), dev(w)
+
+    def run(buf):
+        if dedup:
+            L, *_, h = buf.dispatch_dedup_with_layout(x, td, wd, True)
+        else:
+            L, *_, h = buf.dispatch_with_layout(x, td, wd, True)
+        return L, h, buf.status()
+
+    monkeypatch.setenv("EP_SPIN_LIMIT", "1")
+    buf = ep.Buffer(T, H, k, E, R, cap)
+    _, h, st = run(buf)
+    assert st & ep.EP_ST_TIMEOUT, st
+    p = host(h.pos)
+    assert ((p >= -1) & (p < R * cap)).all()  # whatever it placed is inside the buffer
+    buf.close()
+
+    monkeypatch.delenv("EP_SPIN_LIMIT")
+    buf = ep.Buffer(T, H, k, E, R, cap)
+    L, h, st = run(buf)
+    assert st == 0
+    if dedup:
+        rir_o, _, _ = orc.layout_dedup(topk, E, R, cap)
+        pos_o, _ = orc.positions_dedup(topk, rir_o, E, R, cap)
+        assert np.array_equal(host(L.rank_in_rank), rir_o)
+    else:
+        L2 = orc.layout(topk, E, R, cap)
+        pos_o, _ = orc.positions(topk, L2, E, R, cap)
+        assert np.array_equal(host(L.rank_in_expert), L2.rank_in_expert)
+    assert np.array_equal(host(h.pos), pos_o)
