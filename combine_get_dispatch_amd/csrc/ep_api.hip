@@ -38,7 +38,6 @@ namespace {
 constexpr int kDispatchTargetWaves = 2048;  // ~8 waves per CU on 256 CUs
 constexpr int kCombineTargetWaves = 1 << 30;  // i.e. one pass per wave
 constexpr int kFusedMaxTiles = 16;             // layout tiles up to which one grid does layout + dispatch
-constexpr int64_t kRowsCachedBytes = 320ll << 20;  // row writes up to this use cache-allocating stores
 constexpr int kMaxPassPerWave = 8;   // must match ep_kernels.hip
 
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -188,10 +187,6 @@ int fill_dispatch(ep_ctx *ctx, const uint16_t *x, const int32_t *topk, const flo
     a.waves_per_token = g.wpt;
     a.passes_per_wave = g.ppw;
     a.npass = g.npass;
-    // FP8 rows beyond what the memory-side cache absorbs: non-temporal stores
-    // (BF16 rows measured no faster with them: 2 GB, 462 vs 453 us)
-    const int64_t row_bytes = (int64_t)c.hidden + 4 * (c.hidden / 128);
-    a.nt_rows = recv_scales != nullptr && (int64_t)c.num_tokens * c.num_topk * row_bytes > kRowsCachedBytes;
     a.counters = ctx->counters;
     return EP_OK;
 }

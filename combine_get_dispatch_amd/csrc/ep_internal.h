@@ -62,8 +62,6 @@ struct DispatchArgs {
     int T, k, E, epr, epr_shift, H;
     int64_t cap_rows, num_rows;  // num_rows = R * cap_rows
     int waves_per_token, passes_per_wave, npass;
-    int nt_rows;                 // rows written with non-temporal stores (a call writing more than the MALL
-                                 // holds; separate dispatch launches only)
     uint32_t *counters;
 };
 

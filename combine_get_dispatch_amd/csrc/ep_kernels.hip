@@ -831,15 +831,14 @@ __device__ __forceinline__ void load_rows(const DispatchArgs &a, int t, int part
 }
 
 // Quantize (FP8) or copy (BF16) the wave's passes into the receive rows of
-// its token's kept slots (slot j's row in lane j of p). A call whose rows
-// fit about the 256 MB memory-side cache (MALL) writes them with ordinary
-// stores, which it absorbs (faster); a larger one with non-temporal stores
-// (NT; faster once the cache cannot hold them). Measured on MI355X, FP8
-// rows: 294 MB 60.7 vs 71.9 us, 352 MB 93.1 vs 87.6 us, 940 MB 301 vs 241 us
-// (BF16 rows gained nothing, so the host asks for NT on FP8 rows only).
-// Only the separate dispatch kernel is built both ways; the fused and
-// low-latency kernels, used for smaller calls, store ordinarily.
-template <bool FP8, bool NT = false>
+// its token's kept slots (slot j's row in lane j of p). Rows are written with
+// non-temporal stores. Ordinary stores are faster only while the rows stay
+// in the 256 MB memory-side cache (MALL) from one call to the next, i.e.
+// when the same receive buffer is rewritten with nothing in between; with
+// independent buffers per step (as in a model, where every layer brings new
+// data) the MI355X prefill step is 158.6 us with non-temporal row stores
+// against 171.9 us with ordinary ones, and decode steps are no slower.
+template <bool FP8>
 __device__ __forceinline__ void store_rows(const DispatchArgs &a, int part, int p,
                                            const u32x4 (&v)[2 * kMaxPassPerWave]) {
     const int lane = threadIdx.x & 63;
@@ -895,11 +894,7 @@ __device__ __forceinline__ void store_rows(const DispatchArgs &a, int part, int 
                 const int pj = readlane_i(p, j);
                 if (pj < 0) continue;
                 if (act) {
-                    u32x4 *dst = reinterpret_cast<u32x4 *>(rx + (size_t)pj * H + c);
-                    if (NT)
-                        __builtin_nontemporal_store(qv, dst);
-                    else
-                        *dst = qv;
+                    __builtin_nontemporal_store(qv, reinterpret_cast<u32x4 *>(rx + (size_t)pj * H + c));
                     if ((lane & 7) == 0) a.recv_scales[(size_t)pj * G + (c >> 7)] = scale;
                 }
             }
@@ -911,19 +906,14 @@ __device__ __forceinline__ void store_rows(const DispatchArgs &a, int part, int 
                 const int pj = readlane_i(p, j);
                 if (pj < 0) continue;
                 u32x4 *dst = reinterpret_cast<u32x4 *>(rx + (size_t)pj * H + c0);
-                if (NT) {
-                    if (a0) __builtin_nontemporal_store(v[2 * i], dst);
-                    if (a1) __builtin_nontemporal_store(v[2 * i + 1], dst + 64);
-                } else {
-                    if (a0) *dst = v[2 * i];
-                    if (a1) dst[64] = v[2 * i + 1];
-                }
+                if (a0) __builtin_nontemporal_store(v[2 * i], dst);
+                if (a1) __builtin_nontemporal_store(v[2 * i + 1], dst + 64);
             }
         }
     }
 }
 
-template <bool FP8, int MODE, bool NT>
+template <bool FP8, int MODE>
 __global__ __launch_bounds__(kWavesPerBlock * 64) void k_dispatch(DispatchArgs a) {
     const int gw = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
     const int t = gw / a.waves_per_token;
@@ -932,7 +922,7 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void k_dispatch(DispatchArgs a
     u32x4 v[2 * kMaxPassPerWave];
     load_rows<FP8>(a, t, part, true, v);  // in flight while the slot rows are looked up
     const int p = slot_row<MODE, false>(a, t, threadIdx.x & 63, part);
-    store_rows<FP8, NT>(a, part, p, v);
+    store_rows<FP8>(a, part, p, v);
 }
 
 // Slot j's receive row (lane j) from the layout this block holds in LDS
@@ -1423,32 +1413,22 @@ hipError_t launch_dispatch_inblock(const LayoutArgs &la, const DispatchArgs &da,
     return hipGetLastError();
 }
 
-template <int MODE, bool NT>
+template <int MODE>
 void launch_dispatch_t(const DispatchArgs &a, bool fp8, dim3 grid, dim3 block, hipStream_t s) {
     if (fp8)
-        hipLaunchKernelGGL((k_dispatch<true, MODE, NT>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((k_dispatch<true, MODE>), grid, block, 0, s, a);
     else
-        hipLaunchKernelGGL((k_dispatch<false, MODE, NT>), grid, block, 0, s, a);
-}
-
-template <bool NT>
-void launch_dispatch_nt(const DispatchArgs &a, bool fp8, int mode, dim3 grid, dim3 block, hipStream_t s) {
-    if (mode == kRowsPerExpert)
-        launch_dispatch_t<kRowsPerExpert, NT>(a, fp8, grid, block, s);
-    else if (mode == kRowsPerRank)
-        launch_dispatch_t<kRowsPerRank, NT>(a, fp8, grid, block, s);
-    else
-        launch_dispatch_t<kRowsFromHandle, NT>(a, fp8, grid, block, s);
+        hipLaunchKernelGGL((k_dispatch<false, MODE>), grid, block, 0, s, a);
 }
 
 hipError_t launch_dispatch(const DispatchArgs &a, bool fp8, int mode, int num_waves, hipStream_t s) {
     const dim3 grid((num_waves + kWavesPerBlock - 1) / kWavesPerBlock), block(kWavesPerBlock * 64);
-    // the store policy is a template argument: a runtime branch between the
-    // two stores is merged by the compiler into ordinary stores
-    if (a.nt_rows)
-        launch_dispatch_nt<true>(a, fp8, mode, grid, block, s);
+    if (mode == kRowsPerExpert)
+        launch_dispatch_t<kRowsPerExpert>(a, fp8, grid, block, s);
+    else if (mode == kRowsPerRank)
+        launch_dispatch_t<kRowsPerRank>(a, fp8, grid, block, s);
     else
-        launch_dispatch_nt<false>(a, fp8, mode, grid, block, s);
+        launch_dispatch_t<kRowsFromHandle>(a, fp8, grid, block, s);
     return hipGetLastError();
 }
 
