@@ -111,6 +111,15 @@ int hip_fail(hipError_t e, const char *what) {
     return EP_ERR_HIP;
 }
 
+// The context's workspace lives on the device that was current at
+// ep_create; a call made with another device current would hand its kernels
+// that workspace. (EP_ERR_ARG: make the context's device current.)
+int check_device(const ep_ctx *ctx) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return EP_ERR_HIP;
+    return dev == ctx->device ? EP_OK : EP_ERR_ARG;
+}
+
 int check_handle(const ep_ctx *ctx, const ep_handle *h) {
     if (!h) return EP_ERR_ARG;
     if (h->num_tokens != ctx->cfg.num_tokens || h->num_topk != ctx->cfg.num_topk) return EP_ERR_ARG;
@@ -121,6 +130,7 @@ int check_handle(const ep_ctx *ctx, const ep_handle *h) {
 int combine_common(ep_ctx *ctx, const uint16_t *rows, const ep_handle *h, const float *w, void *out,
                    bool out_f32, ep_stream_t stream, const char *name) {
     if (!ctx) return EP_ERR_ARG;
+    if (int r = check_device(ctx)) return r;
     if (int r = check_handle(ctx, h)) return r;
     const ep_config &c = ctx->cfg;
     if (c.num_tokens == 0) return EP_OK;
@@ -210,6 +220,7 @@ int dispatch_common(ep_ctx *ctx, const uint16_t *x, const int32_t *topk, const f
 
 int fill_layout(ep_ctx *ctx, const int32_t *topk_idx, const ep_layout *L, ep::LayoutArgs &a) {
     if (!ctx || !L) return EP_ERR_ARG;
+    if (int r = check_device(ctx)) return r;
     const ep_config &c = ctx->cfg;
     if (!L->cnt_se || !L->cnt_sd || !L->recv_cnt || !L->expert_off || !L->rank_rows || !L->src_expert_off)
         return EP_ERR_ARG;
@@ -281,6 +292,7 @@ int launch_fused(ep_ctx *ctx, const ep::LayoutArgs &la, const ep::DispatchArgs &
 int check_forward_dispatch(ep_ctx *ctx, const int32_t *topk_idx, const float *topk_weights, const ep_layout *L,
                            int use_fp8, float *recv_scales, float *recv_w, ep_handle *handle) {
     if (!ctx || !L || !handle) return EP_ERR_ARG;
+    if (int r = check_device(ctx)) return r;
     const ep_config &c = ctx->cfg;
     if (use_fp8 != 0 && use_fp8 != 1) return EP_ERR_ARG;
     if (use_fp8 && (c.hidden % 128 || (!recv_scales && c.cap_rows > 0))) return EP_ERR_ARG;
@@ -435,6 +447,7 @@ int ep_dispatch_low_latency(ep_ctx *ctx, const uint16_t *x, const int32_t *topk_
                             int use_fp8, void *recv_x, float *recv_scales, float *recv_w, int32_t *recv_count,
                             ep_handle *handle, ep_stream_t stream) {
     if (!ctx || !handle || !recv_count) return EP_ERR_ARG;
+    if (int r = check_device(ctx)) return r;
     const ep_config &c = ctx->cfg;
     const int T = c.num_tokens, R = c.num_ranks;
     if (use_fp8 != 0 && use_fp8 != 1) return EP_ERR_ARG;
@@ -529,6 +542,7 @@ int ep_combine_f32(ep_ctx *ctx, const uint16_t *expert_out, const ep_handle *han
 int ep_combine_backward(ep_ctx *ctx, const uint16_t *grad_combined, const ep_handle *handle,
                         uint16_t *grad_rows, ep_stream_t stream) {
     if (!ctx) return EP_ERR_ARG;
+    if (int r = check_device(ctx)) return r;
     if (int r = check_handle(ctx, handle)) return r;
     ep_handle h = *handle;
     return dispatch_common(ctx, grad_combined, nullptr, nullptr, nullptr, false, 0, grad_rows, nullptr,
@@ -542,6 +556,7 @@ int ep_dispatch_backward(ep_ctx *ctx, const uint16_t *grad_rows, const ep_handle
 
 int ep_get_status(ep_ctx *ctx, ep_stream_t stream, uint32_t *status) {
     if (!ctx || !status) return EP_ERR_ARG;
+    if (int r = check_device(ctx)) return r;
     int r = hip_fail(hipStreamSynchronize((hipStream_t)stream), "hipStreamSynchronize");
     if (r) return r;
     r = hip_fail(hipMemcpy(status, ctx->counters + ep::kStatus, sizeof(uint32_t), hipMemcpyDeviceToHost),

@@ -38,7 +38,9 @@
  *    kernels never write outside the caller's buffers when one is raised.
  *  - One ep_ctx holds a small device workspace used by the layout kernel;
  *    calls on the same ctx must be ordered on one stream (calls on different
- *    streams that use the same ctx at the same time race).
+ *    streams that use the same ctx at the same time race). A context belongs
+ *    to the device current at ep_create: a call made while another device is
+ *    current returns EP_ERR_ARG.
  */
 #ifndef EP_H
 #define EP_H
