@@ -721,20 +721,64 @@ enum SlotMode { kRowsFromHandle = 0, kRowsPerExpert = 1, kRowsPerRank = 2 };
 // leader slots' ranks, and part 0 of the token also writes each kept row's
 // routing entries. From the handle: the backward pass. In a fused launch the
 // layout was written by other blocks of the same grid, so it is read with
-// coherent (agent-scope) loads.
+// coherent (agent-scope) loads, after the wait for it.
+//
+// Loads and stores complete in issue order, so a wave that waits for one load
+// also waits for every load issued before it. The lookup is therefore split
+// in three: slot_inputs() loads what does not depend on a layout still being
+// written (the routing entry, the weight and, outside a fused grid, the
+// layout's rank) before the wave issues its row loads; slot_loads() issues
+// the layout-dependent loads together (one round trip, not a chain of three);
+// slot_finish() places the rows once they have arrived, with the FP8
+// quantization in between.
+struct SlotIn {
+    int e;    // expert id (per expert, per rank) or the handle's position
+    int r;    // rank within the expert / the rank (not fused), else -1
+    float w;  // the slot's weight, when it is written to a receive buffer
+};
+
+struct SlotLd {
+    int r;   // rank within the expert / the rank
+    int eo;  // the expert's offset (per expert)
+};
+
 template <int MODE, bool FUSED>
-__device__ __forceinline__ int slot_row(const DispatchArgs &a, int t, int lane, int part) {
+__device__ __forceinline__ SlotIn slot_inputs(const DispatchArgs &a, int t, int lane) {
+    SlotIn s{-1, -1, 0.0f};
+    if (lane < a.k) {
+        const size_t i = (size_t)t * a.k + lane;
+        if (MODE == kRowsFromHandle) {
+            s.e = a.pos[i];
+        } else {
+            s.e = a.topk[i];
+            if (MODE == kRowsPerExpert ? a.recv_w != nullptr : a.recv_topk_w != nullptr) s.w = a.w[i];
+            if (!FUSED) s.r = MODE == kRowsPerExpert ? a.rank_in_expert[i] : a.rank_in_rank[i];
+        }
+    }
+    return s;
+}
+
+template <int MODE, bool FUSED>
+__device__ __forceinline__ SlotLd slot_loads(const DispatchArgs &a, int t, int lane, const SlotIn &s) {
+    SlotLd l{s.r, 0};
+    if (MODE == kRowsFromHandle || lane >= a.k) return l;
+    const size_t i = (size_t)t * a.k + lane;
+    const int32_t *ranks = MODE == kRowsPerExpert ? a.rank_in_expert : a.rank_in_rank;
+    if (FUSED) l.r = __hip_atomic_load(ranks + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (MODE == kRowsPerExpert && s.e >= 0 && s.e < a.E)
+        l.eo = FUSED ? __hip_atomic_load(a.expert_off + s.e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                     : a.expert_off[s.e];
+    return l;
+}
+
+template <int MODE>
+__device__ __forceinline__ int slot_finish(const DispatchArgs &a, int t, int lane, int part, const SlotIn &s,
+                                           const SlotLd &l) {
     int p = -1;
     if (MODE == kRowsPerRank) {
         const size_t i = (size_t)t * a.k + lane;
-        int e = -1, rr = -1, d = -1;
-        float wv = 0.0f;
-        if (lane < a.k) {
-            e = a.topk[i];
-            if (a.recv_topk_w) wv = a.w[i];
-            rr = FUSED ? __hip_atomic_load(a.rank_in_rank + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                       : a.rank_in_rank[i];
-        }
+        const int e = s.e, rr = l.r;
+        int d = -1;
         // kept: a valid expert that no earlier slot of the token repeats (the
         // layout's rule), from the slots themselves
         int kept = e >= 0 && e < a.E;
@@ -755,7 +799,7 @@ __device__ __forceinline__ int slot_row(const DispatchArgs &a, int t, int lane, 
             // expert index among rank d's experts, and its weight
             for (int jj = 0; jj < a.k; ++jj) {
                 const int ej = readlane_i(e, jj), kj = readlane_i(kept, jj);
-                const float wj = readlane_f(wv, jj);
+                const float wj = readlane_f(s.w, jj);
                 if (p >= 0) {
                     const bool here = kj && rank_of(ej, a.epr, a.epr_shift) == d;
                     a.recv_topk_idx[(size_t)p * a.k + jj] = here ? ej - d * a.epr : -1;
@@ -768,13 +812,9 @@ __device__ __forceinline__ int slot_row(const DispatchArgs &a, int t, int lane, 
     if (lane < a.k) {
         const size_t i = (size_t)t * a.k + lane;
         if (MODE == kRowsPerExpert) {
-            const int e = a.topk[i];
-            const int r = FUSED ? __hip_atomic_load(a.rank_in_expert + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                                : a.rank_in_expert[i];
+            const int e = s.e, r = l.r;
             if (r >= 0 && e >= 0 && e < a.E) {
-                const int eo = FUSED ? __hip_atomic_load(a.expert_off + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                                     : a.expert_off[e];
-                const int64_t local = (int64_t)eo + r;
+                const int64_t local = (int64_t)l.eo + r;
                 if (local >= 0 && local < a.cap_rows)
                     p = (int)((int64_t)rank_of(e, a.epr, a.epr_shift) * a.cap_rows + local);
             }
@@ -782,11 +822,11 @@ __device__ __forceinline__ int slot_row(const DispatchArgs &a, int t, int lane, 
                 a.pos[i] = p;
                 if (p >= 0) {
                     a.src_idx[p] = t;
-                    if (a.recv_w) a.recv_w[p] = a.w[i];
+                    if (a.recv_w) a.recv_w[p] = s.w;
                 }
             }
         } else {
-            p = a.pos[i];
+            p = s.e;
             if (p < -1 || p >= a.num_rows) {  // not a position this buffer holds
                 atomicOr(&a.counters[kStatus], kStBadHandle);
                 p = -1;
@@ -830,69 +870,75 @@ __device__ __forceinline__ void load_rows(const DispatchArgs &a, int t, int part
     }
 }
 
-// Quantize (FP8) or copy (BF16) the wave's passes into the receive rows of
-// its token's kept slots (slot j's row in lane j of p). Rows are written with
+// FP8: quantize the wave's passes in place (pass i's 16 codes per lane into
+// v[2i], its group scale into sc[i]). BF16 rows are copied as loaded.
+template <bool FP8>
+__device__ __forceinline__ void quantize_rows(const DispatchArgs &a, int part, u32x4 (&v)[2 * kMaxPassPerWave],
+                                              float (&sc)[kMaxPassPerWave]) {
+#pragma unroll
+    for (int i = 0; i < kMaxPassPerWave; ++i) sc[i] = 0.0f;
+    if (!FP8) return;
+    const int np = min(a.passes_per_wave, a.npass - part * a.passes_per_wave);
+#pragma unroll
+    for (int i = 0; i < kMaxPassPerWave; ++i) {
+        if (i >= np) continue;
+        float f[16];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const u32x4 u = v[2 * i + h];
+            f[8 * h + 0] = bf16_lo(u.x);
+            f[8 * h + 1] = bf16_hi(u.x);
+            f[8 * h + 2] = bf16_lo(u.y);
+            f[8 * h + 3] = bf16_hi(u.y);
+            f[8 * h + 4] = bf16_lo(u.z);
+            f[8 * h + 5] = bf16_hi(u.z);
+            f[8 * h + 6] = bf16_lo(u.w);
+            f[8 * h + 7] = bf16_hi(u.w);
+        }
+        float m = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(f[e]));
+        m = dpp_max<0xB1>(m);
+        m = dpp_max<0x4E>(m);
+        m = dpp_max<0x141>(m);
+        const float am = fmaxf(m, 1e-4f);
+        const float inv = 448.0f / am;   // IEEE division
+        sc[i] = am / 448.0f;             // IEEE division
+        uint32_t q[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float y0 = fminf(fmaxf(f[4 * e + 0] * inv, -448.0f), 448.0f);
+            const float y1 = fminf(fmaxf(f[4 * e + 1] * inv, -448.0f), 448.0f);
+            const float y2 = fminf(fmaxf(f[4 * e + 2] * inv, -448.0f), 448.0f);
+            const float y3 = fminf(fmaxf(f[4 * e + 3] * inv, -448.0f), 448.0f);
+            int w = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
+            w = __builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, w, true);
+            q[e] = (uint32_t)w;
+        }
+        v[2 * i] = u32x4{q[0], q[1], q[2], q[3]};
+    }
+}
+
+// Write the wave's passes (quantized for FP8) into the receive rows of its
+// token's kept slots (slot j's row in lane j of p). Rows are written with
 // non-temporal stores. Ordinary stores are faster only while the rows stay
 // in the 256 MB memory-side cache (MALL) from one call to the next, i.e.
 // when the same receive buffer is rewritten with nothing in between; with
 // independent buffers per step (as in a model, where every layer brings new
 // data) the MI355X prefill step is 158.6 us with non-temporal row stores
 // against 171.9 us with ordinary ones, and decode steps are no slower.
-// Each destination row's passes are written back to back (FP8: all passes
-// quantized first), which keeps a row's stores together in the memory queue
-// (1024-token decode step 48.8 vs 50.5 us; prefill unchanged).
+// Each destination row's passes are written back to back, which keeps a
+// row's stores together in the memory queue (1024-token decode step 48.8 vs
+// 50.5 us; prefill unchanged).
 template <bool FP8>
-__device__ __forceinline__ void store_rows(const DispatchArgs &a, int part, int p,
-                                           const u32x4 (&v)[2 * kMaxPassPerWave]) {
+__device__ __forceinline__ void write_rows(const DispatchArgs &a, int part, int p,
+                                           const u32x4 (&v)[2 * kMaxPassPerWave],
+                                           const float (&sc)[kMaxPassPerWave]) {
     const int lane = threadIdx.x & 63;
     const int pass0 = part * a.passes_per_wave;
     const int np = min(a.passes_per_wave, a.npass - pass0);
     const int H = a.H;
     if (FP8) {
-        // quantize every pass first, then write each destination row's
-        // passes back to back
-        u32x4 qv[kMaxPassPerWave];
-        float sc[kMaxPassPerWave];
-#pragma unroll
-        for (int i = 0; i < kMaxPassPerWave; ++i) {
-            qv[i] = 0;
-            sc[i] = 0.0f;
-            if (i >= np) continue;
-            float f[16];
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const u32x4 u = v[2 * i + h];
-                f[8 * h + 0] = bf16_lo(u.x);
-                f[8 * h + 1] = bf16_hi(u.x);
-                f[8 * h + 2] = bf16_lo(u.y);
-                f[8 * h + 3] = bf16_hi(u.y);
-                f[8 * h + 4] = bf16_lo(u.z);
-                f[8 * h + 5] = bf16_hi(u.z);
-                f[8 * h + 6] = bf16_lo(u.w);
-                f[8 * h + 7] = bf16_hi(u.w);
-            }
-            float m = 0.0f;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(f[e]));
-            m = dpp_max<0xB1>(m);
-            m = dpp_max<0x4E>(m);
-            m = dpp_max<0x141>(m);
-            const float am = fmaxf(m, 1e-4f);
-            const float inv = 448.0f / am;   // IEEE division
-            sc[i] = am / 448.0f;             // IEEE division
-            uint32_t q[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float y0 = fminf(fmaxf(f[4 * e + 0] * inv, -448.0f), 448.0f);
-                const float y1 = fminf(fmaxf(f[4 * e + 1] * inv, -448.0f), 448.0f);
-                const float y2 = fminf(fmaxf(f[4 * e + 2] * inv, -448.0f), 448.0f);
-                const float y3 = fminf(fmaxf(f[4 * e + 3] * inv, -448.0f), 448.0f);
-                int w = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
-                w = __builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, w, true);
-                q[e] = (uint32_t)w;
-            }
-            qv[i] = u32x4{q[0], q[1], q[2], q[3]};
-        }
         const int G = H >> 7;
         uint8_t *rx = static_cast<uint8_t *>(a.recv_x);
         for (int j = 0; j < a.k; ++j) {
@@ -903,7 +949,7 @@ __device__ __forceinline__ void store_rows(const DispatchArgs &a, int part, int 
                 if (i >= np) break;
                 const int c = (pass0 + i) * 1024 + lane * 16;
                 if (c < H) {
-                    __builtin_nontemporal_store(qv[i], reinterpret_cast<u32x4 *>(rx + (size_t)pj * H + c));
+                    __builtin_nontemporal_store(v[2 * i], reinterpret_cast<u32x4 *>(rx + (size_t)pj * H + c));
                     if ((lane & 7) == 0) a.recv_scales[(size_t)pj * G + (c >> 7)] = sc[i];
                 }
             }
@@ -925,16 +971,28 @@ __device__ __forceinline__ void store_rows(const DispatchArgs &a, int part, int 
     }
 }
 
+template <bool FP8>
+__device__ __forceinline__ void store_rows(const DispatchArgs &a, int part, int p, u32x4 (&v)[2 * kMaxPassPerWave]) {
+    float sc[kMaxPassPerWave];
+    quantize_rows<FP8>(a, part, v, sc);
+    write_rows<FP8>(a, part, p, v, sc);
+}
+
 template <bool FP8, int MODE>
 __global__ __launch_bounds__(kWavesPerBlock * 64) void k_dispatch(DispatchArgs a) {
     const int gw = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
     const int t = gw / a.waves_per_token;
     const int part = gw - t * a.waves_per_token;
     if (t >= a.T) return;  // whole wave
+    const int lane = threadIdx.x & 63;
+    const SlotIn s = slot_inputs<MODE, false>(a, t, lane);  // issued before the rows
     u32x4 v[2 * kMaxPassPerWave];
-    load_rows<FP8>(a, t, part, true, v);  // in flight while the slot rows are looked up
-    const int p = slot_row<MODE, false>(a, t, threadIdx.x & 63, part);
-    store_rows<FP8>(a, part, p, v);
+    load_rows<FP8>(a, t, part, true, v);
+    const SlotLd l = slot_loads<MODE, false>(a, t, lane, s);  // in flight during the quantization
+    float sc[kMaxPassPerWave];
+    quantize_rows<FP8>(a, part, v, sc);
+    const int p = slot_finish<MODE>(a, t, lane, part, s, l);
+    write_rows<FP8>(a, part, p, v, sc);
 }
 
 // Slot j's receive row (lane j) from the layout this block holds in LDS
@@ -1098,16 +1156,22 @@ __device__ __forceinline__ void fused_dispatch_block(const DispatchArgs &da, con
     const int t = gw / da.waves_per_token;
     const int part = gw - t * da.waves_per_token;
     const bool active = gw < items;  // whole wave
+    const int lane = threadIdx.x & 63;
+    SlotIn s{-1, -1, 0.0f};
+    if (active) s = slot_inputs<MODE, true>(da, t, lane);
     u32x4 v[2 * kMaxPassPerWave];
-    load_rows<FP8>(da, t, part, active, v);  // loaded before the layout is known
+    load_rows<FP8>(da, t, part, active, v);  // loaded and quantized before the layout is known
+    float sc[kMaxPassPerWave];
+    quantize_rows<FP8>(da, part, v, sc);
     // every wave of the block reaches the barrier inside
     const int gw0 = db * NW;
     const int t_first = min(gw0 / da.waves_per_token, da.T - 1);
     const int t_last = min((min(gw0 + NW, items) - 1) / da.waves_per_token, da.T - 1);
     wait_for_layout(lw, t_first, max(t_last, t_first));
     if (active) {
-        const int p = slot_row<MODE, true>(da, t, threadIdx.x & 63, part);
-        store_rows<FP8>(da, part, p, v);
+        const SlotLd l = slot_loads<MODE, true>(da, t, lane, s);
+        const int p = slot_finish<MODE>(da, t, lane, part, s, l);
+        write_rows<FP8>(da, part, p, v, sc);
     }
 }
 
@@ -1188,11 +1252,16 @@ __global__ __launch_bounds__(kTileTokens) void k_layout_dispatch(LayoutArgs la, 
         const int t = gw / da.waves_per_token;
         if (lw < extra) {  // whole wave
             const int part = gw - t * da.waves_per_token;
+            const int lane = threadIdx.x & 63;
+            const SlotIn s = slot_inputs<MODE, true>(da, t, lane);
             u32x4 v[2 * kMaxPassPerWave];
             load_rows<FP8>(da, t, part, true, v);
+            float sc[kMaxPassPerWave];
+            quantize_rows<FP8>(da, part, v, sc);
             wave_wait_for_layout(make_wait(la, epoch, tpb, kTotals), t);
-            const int p = slot_row<MODE, true>(da, t, threadIdx.x & 63, part);
-            store_rows<FP8>(da, part, p, v);
+            const SlotLd l = slot_loads<MODE, true>(da, t, lane, s);
+            const int p = slot_finish<MODE>(da, t, lane, part, s, l);
+            write_rows<FP8>(da, part, p, v, sc);
         }
     } else {
         const uint32_t epoch = load_epoch(la);
