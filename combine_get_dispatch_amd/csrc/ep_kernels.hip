@@ -29,6 +29,11 @@ namespace ep {
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+// Buffer resources (gfx9 family): the fourth descriptor word of a raw,
+// unswizzled buffer of 32-bit elements, and the cache-policy operand of a
+// non-temporal load (bit 1).
+constexpr int kBufferRsrcWord3 = 0x00020000;
+constexpr int kLoadNonTemporal = 2;
 
 constexpr uint32_t kStBad = 1u, kStDup = 2u, kStCap = 4u, kStTimeout = 8u, kStBadHandle = 16u;
 constexpr int kWavesPerBlock = 4;
@@ -761,13 +766,18 @@ __device__ __forceinline__ SlotIn slot_inputs(const DispatchArgs &a, int t, int 
 template <int MODE, bool FUSED>
 __device__ __forceinline__ SlotLd slot_loads(const DispatchArgs &a, int t, int lane, const SlotIn &s) {
     SlotLd l{s.r, 0};
-    if (MODE == kRowsFromHandle || lane >= a.k) return l;
-    const size_t i = (size_t)t * a.k + lane;
+    if (MODE == kRowsFromHandle) return l;
+    // every lane loads, lanes past k and invalid experts from a valid address
+    // (their values are not used): with no branch around the loads, the wait
+    // for them lands at their first use, after the quantization
+    const size_t i = (size_t)t * a.k + min(lane, a.k - 1);
     const int32_t *ranks = MODE == kRowsPerExpert ? a.rank_in_expert : a.rank_in_rank;
     if (FUSED) l.r = __hip_atomic_load(ranks + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (MODE == kRowsPerExpert && s.e >= 0 && s.e < a.E)
-        l.eo = FUSED ? __hip_atomic_load(a.expert_off + s.e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                     : a.expert_off[s.e];
+    if (MODE == kRowsPerExpert) {
+        const int ec = (s.e >= 0 && s.e < a.E) ? s.e : 0;
+        l.eo = FUSED ? __hip_atomic_load(a.expert_off + ec, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                     : a.expert_off[ec];
+    }
     return l;
 }
 
@@ -838,35 +848,34 @@ __device__ __forceinline__ int slot_finish(const DispatchArgs &a, int t, int lan
 
 // The bf16 source of this wave's passes, all loads issued at once (read
 // once: non-temporal). FP8: 16 channels per lane per pass; BF16: two 8-channel
-// vectors per lane, 512 channels apart.
+// vectors per lane, 512 channels apart. The loads go through a buffer
+// resource spanning the token's row (none for an inactive wave): a load
+// beyond it returns zeros without touching memory, so all 2*kMaxPassPerWave
+// loads are issued with no branch around them. Loads complete in issue
+// order, and with a fixed count between them the compiler's waits on the
+// loads issued before the rows (the slots, the weight) no longer wait for
+// the rows themselves.
 template <bool FP8>
 __device__ __forceinline__ void load_rows(const DispatchArgs &a, int t, int part, bool active,
                                           u32x4 (&v)[2 * kMaxPassPerWave]) {
     const int lane = threadIdx.x & 63;
+    // t and active are the same in every lane of the wave
+    const int tu = __builtin_amdgcn_readfirstlane(active ? t : 0);
+    const int bytes = __builtin_amdgcn_readfirstlane(active ? a.H * 2 : 0);
+    const __amdgpu_buffer_rsrc_t row = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(a.x + (size_t)tu * a.H), 0, bytes, kBufferRsrcWord3);
     const int pass0 = part * a.passes_per_wave;
     const int np = min(a.passes_per_wave, a.npass - pass0);
-    const int H = a.H;
-    const uint16_t *xrow = a.x + (size_t)t * H;
 #pragma unroll
     for (int i = 0; i < kMaxPassPerWave; ++i) {
-        v[2 * i] = 0;
-        v[2 * i + 1] = 0;
-        if (active && i < np) {
-            const int ps = pass0 + i;
-            if (FP8) {
-                const int c = ps * 1024 + lane * 16;  // 16 channels per lane
-                if (c < H) {
-                    const u32x4 *src = reinterpret_cast<const u32x4 *>(xrow + c);
-                    v[2 * i] = __builtin_nontemporal_load(src);
-                    v[2 * i + 1] = __builtin_nontemporal_load(src + 1);
-                }
-            } else {
-                const int c0 = ps * 1024 + lane * 8;  // 8 channels per vector, lanes contiguous
-                if (c0 < H) v[2 * i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(xrow + c0));
-                if (c0 + 512 < H)
-                    v[2 * i + 1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(xrow + c0 + 512));
-            }
-        }
+        const int ps = pass0 + i;
+        // byte offsets of the lane's two vectors; past the row when the pass
+        // is not this wave's
+        int o0 = FP8 ? (ps * 1024 + lane * 16) * 2 : (ps * 1024 + lane * 8) * 2;
+        int o1 = FP8 ? o0 + 16 : o0 + 1024;
+        if (i >= np) o0 = o1 = bytes;
+        v[2 * i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(row, o0, 0, kLoadNonTemporal));
+        v[2 * i + 1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(row, o1, 0, kLoadNonTemporal));
     }
 }
 
@@ -988,6 +997,7 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void k_dispatch(DispatchArgs a
     const SlotIn s = slot_inputs<MODE, false>(a, t, lane);  // issued before the rows
     u32x4 v[2 * kMaxPassPerWave];
     load_rows<FP8>(a, t, part, true, v);
+    __builtin_amdgcn_sched_barrier(0);  // every row load issued before the wait for the slots
     const SlotLd l = slot_loads<MODE, false>(a, t, lane, s);  // in flight during the quantization
     float sc[kMaxPassPerWave];
     quantize_rows<FP8>(a, part, v, sc);
