@@ -79,6 +79,7 @@ CASES = [  # T, k, E, R, H, fp8, cap_delta, bad
     (1024, 8, 64, 8, 512, True, -9, True),      # four tiles, capacity drops, bad ids
     (4096, 8, 256, 32, 256, True, 0, False),    # sixteen tiles: fused with flags
     (5120, 6, 60, 4, 136, False, -20, True),    # beyond 16 tiles: two launches; BF16 with a channel tail
+    (100, 4, 32, 4, 9224, False, 0, False),     # BF16 rows ending 8 channels into a pass
 ]
 
 

@@ -232,6 +232,11 @@ EDGE = {
     "tiles_33": dict(T=8448, k=8, E=256, R=32, H=256, fp8=True),
     # experts per rank not a power of two (division instead of a shift)
     "epr_not_pow2": dict(T=1536, k=8, E=192, R=8, H=256, fp8=True),
+    # rows that end inside a wave's 1024-channel pass: the last pass holds
+    # 8 channels (BF16) or one 128-channel group (FP8), so the row loads
+    # beyond the row's end must read nothing and write nothing
+    "bf16_row_ends_in_pass": dict(T=100, k=4, E=32, R=4, H=9224, fp8=False),
+    "fp8_row_ends_in_pass": dict(T=3000, k=6, E=48, R=6, H=1152, fp8=True),
 }
 
 
