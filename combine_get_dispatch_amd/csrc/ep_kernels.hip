@@ -8,10 +8,12 @@
 //               per-source outputs at the boundaries it owns and the last
 //               tile the totals and offsets.
 //   k_dispatch  token-major pack: each wave reads a token's row once with
-//               128-bit non-temporal loads and writes it to the token's k
-//               receive rows with 128-bit stores; in FP8 mode the per-128-channel amax is reduced
-//               across 8 lanes with DPP and the row is packed with
-//               v_cvt_pk_fp8_f32 (OCP e4m3 on gfx950).
+//               128-bit non-temporal buffer loads (no branches, so every wait
+//               on the slot loads issued before them is exact) and writes it
+//               to the token's k receive rows with 128-bit stores; in FP8
+//               mode the per-128-channel amax is reduced across 8 lanes with
+//               DPP and the row is packed with v_cvt_pk_fp8_f32 (OCP e4m3 on
+//               gfx950).
 //   k_combine   token-major gather-reduce: each wave loads the token's k rows
 //               (all slots in flight) and accumulates in fp32 with one fused
 //               multiply-add per slot in slot order, then rounds to bf16.
