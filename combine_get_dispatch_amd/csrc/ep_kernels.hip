@@ -952,6 +952,17 @@ __device__ __forceinline__ void write_rows(const DispatchArgs &a, int part, int 
     if (FP8) {
         const int G = H >> 7;
         uint8_t *rx = static_cast<uint8_t *>(a.recv_x);
+        // the wave's scales gathered so that lane L holds group pass0*8 + L
+        // (pass L/8, group L%8; its value sits in the group's first lane):
+        // one contiguous scale store per row instead of a 32-byte one per pass
+        float scl = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kMaxPassPerWave; ++i) {
+            const float si = __shfl(sc[i], (lane & 7) << 3);
+            if ((lane >> 3) == i) scl = si;
+        }
+        const int gl = pass0 * 8 + lane;
+        const bool scale_lane = lane < np * 8 && gl < G;
         for (int j = 0; j < a.k; ++j) {
             const int pj = readlane_i(p, j);
             if (pj < 0) continue;
@@ -959,11 +970,9 @@ __device__ __forceinline__ void write_rows(const DispatchArgs &a, int part, int 
             for (int i = 0; i < kMaxPassPerWave; ++i) {
                 if (i >= np) break;
                 const int c = (pass0 + i) * 1024 + lane * 16;
-                if (c < H) {
-                    __builtin_nontemporal_store(v[2 * i], reinterpret_cast<u32x4 *>(rx + (size_t)pj * H + c));
-                    if ((lane & 7) == 0) a.recv_scales[(size_t)pj * G + (c >> 7)] = sc[i];
-                }
+                if (c < H) __builtin_nontemporal_store(v[2 * i], reinterpret_cast<u32x4 *>(rx + (size_t)pj * H + c));
             }
+            if (scale_lane) a.recv_scales[(size_t)pj * G + gl] = scl;
         }
     } else {
         uint16_t *rx = static_cast<uint16_t *>(a.recv_x);
