@@ -39,9 +39,11 @@ constexpr int kDispatchTargetWaves = 2048;  // ~8 waves per CU on 256 CUs
 constexpr int kCombineTargetWaves = 1 << 30;  // i.e. one pass per wave
 // The backward's gradient dispatch (rows from the handle, BF16, no layout in
 // the same grid) also runs one pass per wave: on MI355X with rotated buffers
-// 106.9 vs 109.6 us at 4096 tokens x 7168 and 424.8 vs 439.9 us at 16384.
-// (The fused grids must stay within the resident blocks; the low-latency
-// kernel and the forward dispatch gain nothing from more waves.)
+// 106.9 vs 109.6 us at 4096 tokens x 7168 and 424.8 vs 439.9 us at 16384,
+// with the row loader's full set of 16 loads per wave (a build that issued
+// only the wave's 2 took 110 us). (The fused grids must stay within the
+// resident blocks; the low-latency kernel and the forward dispatch gain
+// nothing from more waves.)
 constexpr int kBackwardTargetWaves = 1 << 30;
 constexpr int kFusedMaxTiles = 16;             // layout tiles up to which one grid does layout + dispatch
 constexpr int kMaxPassPerWave = 8;   // must match ep_kernels.hip

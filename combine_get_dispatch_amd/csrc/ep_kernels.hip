@@ -856,8 +856,10 @@ __device__ __forceinline__ int slot_finish(const DispatchArgs &a, int t, int lan
 // loads are issued with no branch around them. Loads complete in issue
 // order, and with a fixed count between them the compiler's waits on the
 // loads issued before the rows (the slots, the weight) no longer wait for
-// the rows themselves.
-template <bool FP8>
+// the rows themselves. PPW (at least the wave's pass count) bounds the loads
+// issued: a pass past it is not loaded at all, so a launch whose waves hold
+// one pass each issues 2 loads, not 2 * kMaxPassPerWave.
+template <bool FP8, int PPW = kMaxPassPerWave>
 __device__ __forceinline__ void load_rows(const DispatchArgs &a, int t, int part, bool active,
                                           u32x4 (&v)[2 * kMaxPassPerWave]) {
     const int lane = threadIdx.x & 63;
@@ -870,6 +872,11 @@ __device__ __forceinline__ void load_rows(const DispatchArgs &a, int t, int part
     const int np = min(a.passes_per_wave, a.npass - pass0);
 #pragma unroll
     for (int i = 0; i < kMaxPassPerWave; ++i) {
+        if (i >= PPW) {
+            v[2 * i] = 0;
+            v[2 * i + 1] = 0;
+            continue;
+        }
         const int ps = pass0 + i;
         // byte offsets of the lane's two vectors; past the row when the pass
         // is not this wave's
@@ -1076,7 +1083,7 @@ __global__ __launch_bounds__(kTileTokens) void k_dispatch_inblock(LayoutArgs la,
 // popcounts and writes its rows. No block waits on another and the context
 // workspace is not used. The first block of each source writes the region
 // counts recv_count[e][s].
-template <int KMAX, bool FP8>
+template <int KMAX, bool FP8, int PPW>
 __global__ __launch_bounds__(kTileTokens) void k_ll_dispatch(DispatchArgs da, int R, int tpr, int bps,
                                                             int32_t *__restrict__ recv_count) {
     extern __shared__ uint64_t ll_lds[];
@@ -1103,7 +1110,7 @@ __global__ __launch_bounds__(kTileTokens) void k_ll_dispatch(DispatchArgs da, in
     }
     const float wslot = (active && part == 0 && lane < da.k && da.recv_w) ? da.w[(size_t)t * da.k + lane] : 0.0f;
     u32x4 v[2 * kMaxPassPerWave];
-    load_rows<FP8>(da, t, part, active, v);
+    load_rows<FP8, PPW>(da, t, part, active, v);
     for (int i = tid; i < nw * da.E; i += kTileTokens) masks[i] = 0;
     uint32_t st = 0;
     int ev[KMAX];
@@ -1555,17 +1562,22 @@ hipError_t launch_ll_dispatch(const DispatchArgs &a, bool fp8, int R, int32_t *r
     const int bps = (tpr * a.waves_per_token + kWavesPerBlock - 1) / kWavesPerBlock;
     const dim3 grid(max(R * bps, 1)), block(kTileTokens);
     const size_t lds = ll_lds_bytes(a.E, a.k, tpr);
-    if (a.k <= 8) {
-        if (fp8)
-            hipLaunchKernelGGL((k_ll_dispatch<8, true>), grid, block, lds, s, a, R, tpr, bps, recv_count);
-        else
-            hipLaunchKernelGGL((k_ll_dispatch<8, false>), grid, block, lds, s, a, R, tpr, bps, recv_count);
-    } else {
-        if (fp8)
-            hipLaunchKernelGGL((k_ll_dispatch<kMaxTopk, true>), grid, block, lds, s, a, R, tpr, bps, recv_count);
-        else
-            hipLaunchKernelGGL((k_ll_dispatch<kMaxTopk, false>), grid, block, lds, s, a, R, tpr, bps, recv_count);
-    }
+    // row loads per wave fixed at compile time: 1, 2, 4 or 8 passes (at
+    // least the wave's own; at 128 tokens x 7168 each wave holds one pass,
+    // and issuing the 14 loads of the 7 passes it does not hold cost 0.4 us
+    // per step on MI355X)
+    const int ppw = a.passes_per_wave;
+    const int sel = (a.k <= 8 ? 0 : 4) + (fp8 ? 0 : 8) + (ppw <= 1 ? 0 : ppw <= 2 ? 1 : ppw <= 4 ? 2 : 3);
+    static void (*const kernels[16])(DispatchArgs, int, int, int, int32_t *) = {
+        k_ll_dispatch<8, true, 1>,          k_ll_dispatch<8, true, 2>,
+        k_ll_dispatch<8, true, 4>,          k_ll_dispatch<8, true, 8>,
+        k_ll_dispatch<kMaxTopk, true, 1>,   k_ll_dispatch<kMaxTopk, true, 2>,
+        k_ll_dispatch<kMaxTopk, true, 4>,   k_ll_dispatch<kMaxTopk, true, 8>,
+        k_ll_dispatch<8, false, 1>,         k_ll_dispatch<8, false, 2>,
+        k_ll_dispatch<8, false, 4>,         k_ll_dispatch<8, false, 8>,
+        k_ll_dispatch<kMaxTopk, false, 1>,  k_ll_dispatch<kMaxTopk, false, 2>,
+        k_ll_dispatch<kMaxTopk, false, 4>,  k_ll_dispatch<kMaxTopk, false, 8>};
+    hipLaunchKernelGGL(kernels[sel], grid, block, lds, s, a, R, tpr, bps, recv_count);
     return hipGetLastError();
 }
 
