@@ -1052,7 +1052,7 @@ __device__ __forceinline__ int slot_row_lds(const DispatchArgs &a, const LayoutL
 // cross-block waits: every block loads its rows, builds the whole layout in
 // LDS (writing its share of the layout outputs, like a replica), and places
 // its rows from there.
-template <int KMAX, bool FP8>
+template <int KMAX, bool FP8, int PPW>
 __global__ __launch_bounds__(kTileTokens) void k_dispatch_inblock(LayoutArgs la, DispatchArgs da) {
     const int gw = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
     const int t = gw / da.waves_per_token;
@@ -1065,7 +1065,7 @@ __global__ __launch_bounds__(kTileTokens) void k_dispatch_inblock(LayoutArgs la,
     load_slots<KMAX>(la, (int)threadIdx.x, raw);
     const float wslot = (active && part == 0 && lane < da.k && da.recv_w) ? da.w[(size_t)t * da.k + lane] : 0.0f;
     u32x4 v[2 * kMaxPassPerWave];
-    load_rows<FP8>(da, t, part, active, v);
+    load_rows<FP8, PPW>(da, t, part, active, v);
     layout_block<KMAX>(la, 0, (int)blockIdx.x, (int)gridDim.x, kLayoutInBlock, raw, 0u);
     __syncthreads();  // the slots and the scan are in LDS
     if (!active) return;
@@ -1508,17 +1508,19 @@ hipError_t launch_dispatch_inblock(const LayoutArgs &la, const DispatchArgs &da,
                                    hipStream_t s) {
     const size_t lds = inblock_lds_bytes(la.E + la.R, la.k);
     const dim3 grid((num_waves + kWavesPerBlock - 1) / kWavesPerBlock), block(kTileTokens);
-    if (la.k <= 8) {
-        if (fp8)
-            hipLaunchKernelGGL((k_dispatch_inblock<8, true>), grid, block, lds, s, la, da);
-        else
-            hipLaunchKernelGGL((k_dispatch_inblock<8, false>), grid, block, lds, s, la, da);
-    } else {
-        if (fp8)
-            hipLaunchKernelGGL((k_dispatch_inblock<kMaxTopk, true>), grid, block, lds, s, la, da);
-        else
-            hipLaunchKernelGGL((k_dispatch_inblock<kMaxTopk, false>), grid, block, lds, s, la, da);
-    }
+    // row loads per wave fixed at compile time, as in the low-latency kernel
+    const int ppw = da.passes_per_wave;
+    const int sel = (la.k <= 8 ? 0 : 4) + (fp8 ? 0 : 8) + (ppw <= 1 ? 0 : ppw <= 2 ? 1 : ppw <= 4 ? 2 : 3);
+    static void (*const kernels[16])(LayoutArgs, DispatchArgs) = {
+        k_dispatch_inblock<8, true, 1>,         k_dispatch_inblock<8, true, 2>,
+        k_dispatch_inblock<8, true, 4>,         k_dispatch_inblock<8, true, 8>,
+        k_dispatch_inblock<kMaxTopk, true, 1>,  k_dispatch_inblock<kMaxTopk, true, 2>,
+        k_dispatch_inblock<kMaxTopk, true, 4>,  k_dispatch_inblock<kMaxTopk, true, 8>,
+        k_dispatch_inblock<8, false, 1>,        k_dispatch_inblock<8, false, 2>,
+        k_dispatch_inblock<8, false, 4>,        k_dispatch_inblock<8, false, 8>,
+        k_dispatch_inblock<kMaxTopk, false, 1>, k_dispatch_inblock<kMaxTopk, false, 2>,
+        k_dispatch_inblock<kMaxTopk, false, 4>, k_dispatch_inblock<kMaxTopk, false, 8>};
+    hipLaunchKernelGGL(kernels[sel], grid, block, lds, s, la, da);
     return hipGetLastError();
 }
 
