@@ -651,15 +651,29 @@ def cpu_baseline(path, seconds):
         el = time.perf_counter() - t0
         if el >= seconds or steps >= 50:
             break
+    # the backward pair on the last step's positions (bf16 gradients: x as
+    # the gradient of the combined tokens, the expert outputs as the rows')
+    bwd = {"combine_backward": [], "dispatch_backward": []}
+    for _ in range(3):
+        a = time.perf_counter()
+        orc.combine_backward(wl.x, pos, n)
+        b = time.perf_counter()
+        orc.dispatch_backward(eo, pos, wl.topk_w)
+        bwd["combine_backward"].append(b - a)
+        bwd["dispatch_backward"].append(time.perf_counter() - b)
     if old_aff is not None:
         os.sched_setaffinity(0, old_aff)
-    d, c, _ = algo_bytes(cfg.T, cfg.k, cfg.H, nk, cfg.use_fp8)
+    d, c, cb = algo_bytes(cfg.T, cfg.k, cfg.H, nk, cfg.use_fp8)
     per_step = el / steps
+    bmed = {k: sorted(v)[1] for k, v in bwd.items()}
     return {"value": round((d + c) / per_step / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{steps} whole {cfg.name} steps (layout+positions+dispatch+combine, "
-                      f"T={cfg.T}), {per_step * 1e3:.1f} ms/step, single-threaded C oracle on one pinned core",
+                      f"T={cfg.T}), {per_step * 1e3:.1f} ms/step, single-threaded C oracle on one pinned core; "
+                      "then 3 runs of the backward pair",
             "ms_per_step": round(per_step * 1e3, 2),
-            "median_ms": {k: round(sorted(v)[len(v) // 2] * 1e3, 2) for k, v in ops.items()},
+            "median_ms": {**{k: round(sorted(v)[len(v) // 2] * 1e3, 2) for k, v in ops.items()},
+                          **{k: round(v * 1e3, 2) for k, v in bmed.items()}},
+            "backward_GBps": round((cb + c) / sum(bmed.values()) / 1e9, 3),
             "host": {"cpu": cpu_model(), "nproc": os.cpu_count()}}
 
 
