@@ -97,6 +97,10 @@ LL_EDGE = {
     "E_equals_R": dict(T=640, k=4, E=8, R=8, H=512, fp8=True),
     "hidden_16k_bf16": dict(T=64, k=4, E=16, R=4, H=16384, fp8=False),
     "no_weights": dict(T=512, k=8, E=64, R=8, H=256, fp8=True, weights=False),
+    # waves of 2 and 7 passes (the kernel's 2- and 8-pass row loads; 1 and 4
+    # are the decode shapes above)
+    "passes_2": dict(T=512, k=8, E=64, R=8, H=7168, fp8=True),
+    "passes_7_bf16": dict(T=2048, k=4, E=32, R=8, H=7168, fp8=False),
 }
 
 

@@ -237,6 +237,11 @@ EDGE = {
     # beyond the row's end must read nothing and write nothing
     "bf16_row_ends_in_pass": dict(T=100, k=4, E=32, R=4, H=9224, fp8=False),
     "fp8_row_ends_in_pass": dict(T=3000, k=6, E=48, R=6, H=1152, fp8=True),
+    # one tile (the in-block kernel when fused) with waves of 2, 4 and 8
+    # passes: every row-load count the in-block kernel is built for
+    "one_tile_2_passes_bf16": dict(T=256, k=4, E=32, R=4, H=16384, fp8=False),
+    "one_tile_4_passes": dict(T=256, k=4, E=32, R=4, H=32768, fp8=True),
+    "one_tile_8_passes": dict(T=256, k=2, E=16, R=4, H=65536, fp8=True),
 }
 
 
