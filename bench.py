@@ -11,8 +11,9 @@ captured in a HIP graph (up to 10 per graph) and replayed to run exactly K
 (--eager: plain launches; --separate: three calls). `value` is dispatch + combine algorithmic bytes per
 second of step time (GB/s); the JSON line also carries the eager step, the
 per-kernel breakdown (events around eager launches), the roofline of the
-dominant kernel, the decode latency at 128 tokens, the backward pair, and
-the CPU oracle baseline.
+dominant kernel, the decode latency at 128 tokens, the backward pair, the
+skewed and large workloads' steps (`other_workloads`), and the CPU oracle
+baseline.
 """
 from __future__ import annotations
 
@@ -987,6 +988,46 @@ def main():
     if not args.no_extras:
         out["cu_cap_overlap"] = cu_cap_overlap(torch, ep, main_path, K, W)
         print("# overlap: " + json.dumps(out["cu_cap_overlap"]), file=sys.stderr, flush=True)
+
+    if not args.no_extras and cfg.name == "prefill" and not (args.ll or args.dedup or args.tokens_per_rank):
+        # the other full-size workloads: the skewed routing (the metric's
+        # second case) and the large BF16 one with its backward pair, each
+        # the fused step over rotated sets replayed from a HIP graph, as above
+        out["other_workloads"] = {}
+        for wname in ("skewed", "large"):
+            wcfg = workloads.CONFIGS[wname]
+            wd0, wc0, _ = algo_bytes(wcfg.T, wcfg.k, wcfg.H, wcfg.T * wcfg.k, wcfg.use_fp8)
+            wn = max(1, min(16, -(-(2 << 30) // max(wd0 + wc0, 1))))
+            wps = [Path(wcfg, args.seed + i, torch, ep, workloads) for i in range(wn)]
+            wms, _, _ = graph_rotating(torch, [[q.fused_op, q.combine_op] for q in wps], K, W)
+            wN = wps[0].kept_slots()
+            wd, wc, wcb = algo_bytes(wcfg.T, wcfg.k, wcfg.H, wN, wcfg.use_fp8)
+            entry = {"us_per_step": round(wms * 1e3, 2), "GBps": round((wd + wc) / (wms * 1e-3) / 1e9, 1),
+                     "pct_of_hbm_peak": round(100.0 * (wd + wc) / (wms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+                     "tokens": wcfg.T, "ranks_simulated": wcfg.R, "routing": wcfg.routing,
+                     "fp8_dispatch": wcfg.use_fp8, "kept_slots": wN, "cap_rows": wps[0].cap, "rotated_sets": wn}
+            if wcfg.backward:
+                q = wps[0]
+                gy = workloads.device_normal_bf16((wcfg.T, wcfg.H), seed=args.seed + 303)
+                grows = torch.empty((q.buf.num_rows, wcfg.H), dtype=torch.bfloat16, device="cuda")
+                gx = torch.empty((wcfg.T, wcfg.H), dtype=torch.bfloat16, device="cuda")
+                bms, (cb_ms, db_ms) = timed(torch, [lambda: q.buf.combine_backward(gy, q.handle, out=grows),
+                                                    lambda: q.buf.dispatch_backward(q.expert_out, q.handle, q.w,
+                                                                                    out=gx)], K, W)
+                entry["backward"] = {"us_per_step": round(bms * 1e3, 2),
+                                     "combine_backward_us": round(cb_ms * 1e3, 2),
+                                     "dispatch_backward_us": round(db_ms * 1e3, 2),
+                                     "GBps": round((wcb + wc) / (bms * 1e-3) / 1e9, 1)}
+                del gy, grows, gx
+            for q in wps:
+                if q.buf.status():
+                    raise SystemExit(f"bench: device status {q.buf.status()} on {wname}")
+                q.buf.close()
+            del wps
+            torch.cuda.empty_cache()
+            out["other_workloads"][wname] = entry
+            print(f"# {wname}: {entry['us_per_step']:.1f} us/step, {entry['GBps']:.0f} GB/s", file=sys.stderr,
+                  flush=True)
 
     if not args.no_extras and not args.no_decode:
         # decode latency: 128 tokens (one rank's share) and the 8-rank group.
