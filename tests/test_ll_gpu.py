@@ -101,6 +101,7 @@ LL_EDGE = {
     # are the decode shapes above)
     "passes_2": dict(T=512, k=8, E=64, R=8, H=7168, fp8=True),
     "passes_7_bf16": dict(T=2048, k=4, E=32, R=8, H=7168, fp8=False),
+    "passes_7_fp8": dict(T=2048, k=8, E=64, R=8, H=7168, fp8=True),
 }
 
 

@@ -242,6 +242,7 @@ EDGE = {
     "one_tile_2_passes_bf16": dict(T=256, k=4, E=32, R=4, H=16384, fp8=False),
     "one_tile_4_passes": dict(T=256, k=4, E=32, R=4, H=32768, fp8=True),
     "one_tile_8_passes": dict(T=256, k=2, E=16, R=4, H=65536, fp8=True),
+    "one_tile_8_passes_bf16": dict(T=256, k=2, E=16, R=4, H=65536, fp8=False),
 }
 
 
