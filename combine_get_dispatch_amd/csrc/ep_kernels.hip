@@ -1174,10 +1174,11 @@ __global__ __launch_bounds__(kTileTokens) void k_ll_dispatch(DispatchArgs da, in
 }
 
 // The dispatch side of a fused grid with flags: the block's NW waves load
-// (and, for FP8, later quantize) their rows before the layout is known, wait
-// for the layout blocks of their tokens and for the totals, then write the
-// rows. `db` is the block's index among the dispatch blocks, which take the
-// work items [0, items).
+// their routing entries and rows and (FP8) quantize the rows before the
+// layout is known, wait for the layout blocks of their tokens and for the
+// totals, load their slots' ranks and expert offsets together, then write
+// the rows. `db` is the block's index among the dispatch blocks, which take
+// the work items [0, items).
 template <bool FP8, int NW, int MODE>
 __device__ __forceinline__ void fused_dispatch_block(const DispatchArgs &da, const LayoutWait &lw, int db, int items) {
     const int gw = db * NW + (int)(threadIdx.x >> 6);
