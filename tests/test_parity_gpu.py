@@ -481,3 +481,60 @@ def test_graph_replay_matches_eager(fused, cfg_name):
         for a_, b_ in zip(got, ref):
             assert np.array_equal(a_, b_), f"replay {r} differs"
     assert buf.status() == 0
+
+
+# ---------------------------------------------------------------------------
+# two contexts at once: each has its own workspace, epoch and flags
+# ---------------------------------------------------------------------------
+
+def test_two_contexts_on_two_streams_concurrently():
+    """Fused layout+dispatch and combine of two contexts (4 and 16 layout
+    tiles) enqueued alternately on two streams, three times over: every
+    output equals the same context's sequential run bit for bit, and the
+    sequential handles equal the oracle's."""
+    orc = oracle.default()
+    shapes = [replace(CONFIGS["decode"], H=1024), replace(CONFIGS["prefill"], H=512)]
+    runs = []
+    for i, cfg in enumerate(shapes):
+        wl = make_workload(cfg, seed=30 + i)
+        cap = oracle_cap(wl.topk_idx, cfg.E, cfg.R)
+        L = orc.layout(wl.topk_idx, cfg.E, cfg.R, cap)
+        pos_o, src_o = orc.positions(wl.topk_idx, L, cfg.E, cfg.R, cap)
+        buf = ep.Buffer(cfg.T, cfg.H, cfg.k, cfg.E, cfg.R, cap)
+        x, topk, w = dev_bf16(wl.x), dev(wl.topk_idx), dev(wl.topk_w)
+        eo = device_normal_bf16((buf.num_rows, cfg.H), seed=40 + i)
+        layout, rx, rs, rw, h = buf.dispatch_with_layout(x, topk, w, cfg.use_fp8)
+        y = buf.combine(eo, h, w)
+        # the reference: the same calls on zeroed outputs (rows no slot maps
+        # to are never written, so they keep what the buffer held)
+        rx.zero_()
+        y.zero_()
+        buf.dispatch_with_layout(x, topk, w, cfg.use_fp8, layout=layout, out=(rx, rs, rw, h))
+        buf.combine(eo, h, w, out=y)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(h.pos), pos_o)
+        ref = [t.clone() for t in (rx, h.pos, y)]
+        runs.append(dict(cfg=cfg, buf=buf, x=x, topk=topk, w=w, eo=eo, layout=layout,
+                         out=(rx, rs, rw, h), y=y, ref=ref))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for s_ in streams:
+        s_.wait_stream(torch.cuda.current_stream())
+    for _ in range(3):
+        for r in runs:
+            r["out"][0].zero_()
+            r["y"].zero_()
+        torch.cuda.synchronize()
+        for r, s_ in zip(runs, streams):
+            with torch.cuda.stream(s_):
+                r["buf"].dispatch_with_layout(r["x"], r["topk"], r["w"], r["cfg"].use_fp8, layout=r["layout"],
+                                              out=r["out"])
+        for r, s_ in zip(runs, streams):
+            with torch.cuda.stream(s_):
+                r["buf"].combine(r["eo"], r["out"][3], r["w"], out=r["y"])
+        torch.cuda.synchronize()
+        for r in runs:
+            got = (r["out"][0], r["out"][3].pos, r["y"])
+            for a_, b_ in zip(got, r["ref"]):
+                assert torch.equal(a_, b_)
+    for r in runs:
+        assert r["buf"].status() == 0
