@@ -8,8 +8,9 @@
 //               per-source outputs at the boundaries it owns and the last
 //               tile the totals and offsets.
 //   k_dispatch  token-major pack: each wave reads a token's row once with
-//               128-bit non-temporal buffer loads (no branches, so every wait
-//               on the slot loads issued before them is exact) and writes it
+//               128-bit non-temporal loads (branch-free buffer loads, so every
+//               wait on the slot loads issued before them is exact; the
+//               per-expert FP8 form issues them per pass) and writes it
 //               to the token's k receive rows with 128-bit stores; in FP8
 //               mode the per-128-channel amax is reduced across 8 lanes with
 //               DPP and the row is packed with v_cvt_pk_fp8_f32 (OCP e4m3 on
@@ -888,6 +889,46 @@ __device__ __forceinline__ void load_rows(const DispatchArgs &a, int t, int part
     }
 }
 
+// The same loads with a wave-uniform branch per pass and a per-lane bounds
+// test, so only the passes and vectors inside the row are issued, one
+// branch apart, and the compiler's waits after them are for everything
+// issued. In the forward per-expert FP8 dispatch run after a complete
+// layout, which is bound by the HBM write rate of its scattered rows, this
+// slower issue measured 60.2-61.2 us against 62.6-63.5 us for the
+// branch-free loads at 4096 tokens x 7168 top-8 (same GPU, interleaved
+// runs). The rank-deduplicated and gradient dispatches measured slower with
+// it, and the fused and low-latency grids need the exact waits, so they keep
+// the branch-free loader.
+template <bool FP8>
+__device__ __forceinline__ void load_rows_paced(const DispatchArgs &a, int t, int part,
+                                                u32x4 (&v)[2 * kMaxPassPerWave]) {
+    const int lane = threadIdx.x & 63;
+    const int pass0 = part * a.passes_per_wave;
+    const int np = min(a.passes_per_wave, a.npass - pass0);
+    const int H = a.H;
+    const uint16_t *xrow = a.x + (size_t)t * H;
+#pragma unroll
+    for (int i = 0; i < kMaxPassPerWave; ++i) {
+        v[2 * i] = 0;
+        v[2 * i + 1] = 0;
+        if (i >= np) continue;
+        const int ps = pass0 + i;
+        if (FP8) {
+            const int c = ps * 1024 + lane * 16;
+            if (c < H) {
+                const u32x4 *src = reinterpret_cast<const u32x4 *>(xrow + c);
+                v[2 * i] = __builtin_nontemporal_load(src);
+                v[2 * i + 1] = __builtin_nontemporal_load(src + 1);
+            }
+        } else {
+            const int c0 = ps * 1024 + lane * 8;
+            if (c0 < H) v[2 * i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(xrow + c0));
+            if (c0 + 512 < H)
+                v[2 * i + 1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(xrow + c0 + 512));
+        }
+    }
+}
+
 // FP8: quantize the wave's passes in place (pass i's 16 codes per lane into
 // v[2i], its group scale into sc[i]). BF16 rows are copied as loaded.
 template <bool FP8>
@@ -1012,14 +1053,24 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void k_dispatch(DispatchArgs a
     const int part = gw - t * a.waves_per_token;
     if (t >= a.T) return;  // whole wave
     const int lane = threadIdx.x & 63;
-    const SlotIn s = slot_inputs<MODE, false>(a, t, lane);  // issued before the rows
     u32x4 v[2 * kMaxPassPerWave];
-    load_rows<FP8>(a, t, part, true, v);
-    __builtin_amdgcn_sched_barrier(0);  // every row load issued before the wait for the slots
-    const SlotLd l = slot_loads<MODE, false>(a, t, lane, s);  // in flight during the quantization
     float sc[kMaxPassPerWave];
-    quantize_rows<FP8>(a, part, v, sc);
-    const int p = slot_finish<MODE>(a, t, lane, part, s, l);
+    int p;
+    if constexpr (FP8 && MODE == kRowsPerExpert) {
+        // rows first, then the slots (see load_rows_paced)
+        load_rows_paced<FP8>(a, t, part, v);
+        const SlotIn s = slot_inputs<MODE, false>(a, t, lane);
+        const SlotLd l = slot_loads<MODE, false>(a, t, lane, s);
+        p = slot_finish<MODE>(a, t, lane, part, s, l);
+        quantize_rows<FP8>(a, part, v, sc);
+    } else {
+        const SlotIn s = slot_inputs<MODE, false>(a, t, lane);  // issued before the rows
+        load_rows<FP8>(a, t, part, true, v);
+        __builtin_amdgcn_sched_barrier(0);  // every row load issued before the wait for the slots
+        const SlotLd l = slot_loads<MODE, false>(a, t, lane, s);  // in flight during the quantization
+        quantize_rows<FP8>(a, part, v, sc);
+        p = slot_finish<MODE>(a, t, lane, part, s, l);
+    }
     write_rows<FP8>(a, part, p, v, sc);
 }
 
