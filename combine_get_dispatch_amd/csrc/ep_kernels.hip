@@ -16,7 +16,9 @@
 //               DPP and the row is packed with v_cvt_pk_fp8_f32 (OCP e4m3 on
 //               gfx950).
 //   k_combine   token-major gather-reduce: each wave loads the token's k rows
-//               (all slots in flight) and accumulates in fp32 with one fused
+//               (all slots in flight, branch-free buffer loads, so each
+//               slot's arithmetic waits only for its own rows) and
+//               accumulates in fp32 with one fused
 //               multiply-add per slot in slot order, then rounds to bf16.
 //   k_copy      plain 128-bit streaming copy (bandwidth calibration).
 //   k_cu_census the compute unit each workgroup runs on (checks stream CU masks).
@@ -1397,13 +1399,17 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void k_combine(CombineArgs a) 
                 const int j = jb + jj;
                 pj[jj] = j < a.k ? readlane_i(p, j) : -1;
                 wj[jj] = readlane_f(wt, j & 63);
-                r0[jj] = 0;
-                r1[jj] = 0;
-                if (pj[jj] >= 0) {
-                    const uint16_t *src = a.rows + (size_t)pj[jj] * H + c0;
-                    if (a0) r0[jj] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src));
-                    if (a1) r1[jj] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src + 512));
-                }
+                // the slot's row as a buffer resource (none for an empty
+                // slot): a vector past it reads zeros without touching
+                // memory, so every load is issued with no branch around it
+                // and each slot's multiply-adds wait only for that slot
+                const int pr = max(pj[jj], 0);
+                const __amdgpu_buffer_rsrc_t row = __builtin_amdgcn_make_buffer_rsrc(
+                    const_cast<uint16_t *>(a.rows + (size_t)pr * H), 0, pj[jj] >= 0 ? H * 2 : 0, kBufferRsrcWord3);
+                r0[jj] = __builtin_bit_cast(u32x4,
+                                            __builtin_amdgcn_raw_buffer_load_b128(row, c0 * 2, 0, kLoadNonTemporal));
+                r1[jj] = __builtin_bit_cast(
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(row, c0 * 2 + 1024, 0, kLoadNonTemporal));
             }
 #pragma unroll
             for (int jj = 0; jj < kSlotChunk; ++jj) {
