@@ -204,7 +204,7 @@ def brute_layout(topk, E, R, cap):
     recv = np.array([sum(1 for t in range(T) if e in experts_of[t]) for e in range(E)])
     eoff = np.array([sum(int(recv[x]) for x in range((e // epr) * epr, e)) for e in range(E)])
     rrows = np.array([sum(int(recv[e]) for e in range(d * epr, (d + 1) * epr)) for d in range(R)])
-    seoff = np.array([[sum(int(cnt_se[sp, e]) for sp in range(s)) for e in range(E)]
+    seoff = np.array([[int(eoff[e]) + sum(int(cnt_se[sp, e]) for sp in range(s)) for e in range(E)]
                       for s in range(R)])
     if any(int(r) > cap for r in rrows):
         status |= 4
@@ -303,10 +303,11 @@ def check_layout_invariants(topk, E, R, cap, L, pos, src_idx):
     for ee in np.unique(e):
         rows = np.sort(p[e == ee])
         assert np.all(np.diff(src_idx[rows]) > 0), f"expert {ee} rows not in token order"
-    # src_expert_off: inside expert e's rows, those of source rank s start there
+    # src_expert_off: inside rank d(e)'s region, the rows source rank s sends
+    # to expert e start there
     tpr = T // R if T else 1
     for s_, ee, pp in zip(tok[valid] // tpr, e, local):
-        lo = L.expert_off[ee] + L.src_expert_off[s_, ee]
+        lo = L.src_expert_off[s_, ee]
         assert lo <= pp < lo + L.cnt_se[s_, ee]
 
 
@@ -721,8 +722,9 @@ def brute_ll(topk, E, R):
 
 def pin_ll_bruteforce(orc):
     """Brute force, and agreement with the per-expert layout: a region holds
-    cnt_se[s][e] rows, and a slot's row inside it is its rank among expert e's
-    rows less the rows of earlier sources (rank_in_expert - src_expert_off)."""
+    cnt_se[s][e] rows, and a slot's row inside it is its rank-local row in the
+    per-expert layout less where its source's rows start there
+    (expert_off + rank_in_expert - src_expert_off)."""
     rng = np.random.default_rng(61)
     for T, k, E, R in ((32, 4, 16, 4), (40, 6, 24, 8), (24, 8, 8, 2), (9, 3, 6, 3)):
         topk = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32)
@@ -743,7 +745,8 @@ def pin_ll_bruteforce(orc):
                 assert (p >= 0) == (L.rank_in_expert[t, j] >= 0)
                 if p >= 0:
                     e = topk[t, j]
-                    assert p - e * R * tpr - s * tpr == L.rank_in_expert[t, j] - L.src_expert_off[s, e]
+                    assert (p - e * R * tpr - s * tpr ==
+                            L.expert_off[e] + L.rank_in_expert[t, j] - L.src_expert_off[s, e])
 
 
 def pin_ll_invariants(orc):
