@@ -231,17 +231,18 @@ struct TileView {
     uint32_t epoch;
     bool single;
     int replica, nrep, t0, ntile, first_lo, first_hi;
-    bool publish;
 };
 
 // Decoupled look-back of one key, a window of predecessors per round trip:
 // add counts from the nearest predecessor back to the first inclusive
 // prefix; a predecessor that has not published yet ends the window and is
-// read again. Then this tile's share of the key's per-source outputs:
-// prefixes at the source-rank boundaries it owns (boundary s = token s*T/R):
-// src_expert_off directly, and a copy for later tiles. The tile's stores
-// come after its look-back loads (stores and loads share one in-order
-// completion counter).
+// read again. Then this tile's share of the key's per-source outputs: one
+// tile writes the per-source counts itself; several tiles store the key's
+// prefix at each source-rank boundary they own (boundary s = token s*T/R)
+// for the tiles that end those sources and for the last tile, which turns
+// the expert keys' prefixes into src_expert_off. The tile's stores come
+// after its look-back loads (stores and loads share one in-order completion
+// counter).
 __device__ __forceinline__ void lookback_key(const TileView &v, int key) {
     const LayoutArgs &a = v.a;
     const int K = v.K;
@@ -288,24 +289,19 @@ __device__ __forceinline__ void lookback_key(const TileView &v, int key) {
     const bool is_expert = key < a.E;
     const KeyView kv = key_view(v.masks, K, key);
     if (v.single) {
-        // every boundary is here: per-source counts and offsets at once,
-        // the replicas taking the source ranks in turn
+        // every boundary is here: per-source counts at once, the replicas
+        // taking the source ranks in turn
         for (int s = v.replica; s < a.R; s += v.nrep) {
             const int lo = count_before(kv, s * a.tpr, v.ntile);
             const int hi = count_before(kv, (s + 1) * a.tpr, v.ntile);
-            if (is_expert) {
+            if (is_expert)
                 a.cnt_se[(size_t)s * a.E + key] = hi - lo;
-                a.src_expert_off[(size_t)s * a.E + key] = lo;
-            } else {
+            else
                 a.cnt_sd[(size_t)s * a.R + (key - a.E)] = hi - lo;
-            }
         }
     } else {
-        for (int s = v.first_lo; s < v.first_hi; ++s) {
-            const int pre = sum + count_before(kv, s * a.tpr - v.t0, v.ntile);
-            if (is_expert) a.src_expert_off[(size_t)s * a.E + key] = pre;
-            if (v.publish && s == v.first_hi - 1) a.bp[(size_t)s * K + key] = pre;
-        }
+        for (int s = v.first_lo; s < v.first_hi; ++s)
+            store_agent(a.bp + (size_t)s * K + key, sum + count_before(kv, s * a.tpr - v.t0, v.ntile));
     }
 }
 
@@ -338,15 +334,14 @@ __device__ __forceinline__ void layout_block(const LayoutArgs &a, int tile, int 
     // first_hi), and the counts of those whose last token it holds,
     // [last_lo, last_hi); a source inside one tile needs nothing from others.
     int first_lo = 0, first_hi = 0, last_lo = 0, last_hi = 0;
-    bool publish = false;  // a later tile ends a source that starts here
     if (!single) {
         first_lo = min((t0 + a.tpr - 1) / a.tpr, a.R);
         first_hi = min((t0 + kTileTokens + a.tpr - 1) / a.tpr, a.R);
         last_lo = min(t0 / a.tpr, a.R);
         last_hi = min((t0 + kTileTokens) / a.tpr, a.R);
         if (last_tile) last_hi = a.R;
-        publish = first_hi > first_lo && first_hi * a.tpr - 1 >= t0 + kTileTokens;
     }
+    const bool owns = first_hi > first_lo;  // boundary prefixes to publish (several tiles)
 
     // each wave clears its own masks (LDS operations of a wave are ordered):
     // no barrier before the atomics
@@ -395,8 +390,7 @@ __device__ __forceinline__ void layout_block(const LayoutArgs &a, int tile, int 
     if (st && replica == 0) atomicOr(&a.counters[kStatus], st);
     __syncthreads();
 
-    const TileView tv{a, masks, agg, excl, K, tile, epoch, single, replica, nrep, t0, ntile,
-                      first_lo, first_hi, publish};
+    const TileView tv{a, masks, agg, excl, K, tile, epoch, single, replica, nrep, t0, ntile, first_lo, first_hi};
     const bool dedup = a.token_rows != nullptr;  // deduplicated rows asked for
 
     // The rank keys: masks (a token is on rank d if one of its kept slots'
@@ -496,9 +490,10 @@ __device__ __forceinline__ void layout_block(const LayoutArgs &a, int tile, int 
     // 4. the last tile holds every key's total (its look-back is done): rows
     //    per expert, expert offsets inside each rank (block scan), rows per
     //    rank. Replica 0 writes them, before its own ranks and per-source
-    //    counts, which nothing waits on as long; in-block copies keep the
-    //    scan to place their own slots.
-    if (last_tile && (replica == 0 || inblock)) {
+    //    counts, which nothing waits on as long; the other copies of a single
+    //    tile keep the scan for their share of src_expert_off (step 8), and
+    //    in-block copies to place their own slots.
+    if (last_tile && (replica == 0 || single)) {
         const int chunk = (a.E + kTileTokens - 1) / kTileTokens;
         const int lo = min(tid * chunk, a.E), hi = min(lo + chunk, a.E);
         int local = 0;
@@ -595,22 +590,14 @@ __device__ __forceinline__ void layout_block(const LayoutArgs &a, int tile, int 
     }
 
     // 6. the rank keys (unless done first, see above), then the boundary
-    //    prefixes of a source that ends in a later tile, published once both
-    //    kinds of keys have theirs; the workspace is re-armed once the last
-    //    tile has seen every tile's counts (a tile publishes only after
-    //    reading the epoch; fused grids re-arm when their last block ends)
+    //    prefixes this tile owns, published once both kinds of keys have
+    //    stored theirs (each thread waits for its own agent-scope stores
+    //    before the barrier that precedes the flag). The workspace is re-armed
+    //    by the last block of the grid to finish.
     if (!rank_first) rank_keys();
-    if (publish) __threadfence();  // every wave's prefix stores complete before the flag
+    if (owns) wait_own_stores();
     __syncthreads();
-    if (!single && tid == 0) {
-        if (publish) __hip_atomic_store(a.bp_ready + tile, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (!fused && last_tile) {
-            uint32_t ne = (epoch + 1u) & ((1u << 30) - 1u);
-            if (ne == 0) ne = 1;
-            __hip_atomic_store(&a.counters[kTicket], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&a.counters[kEpoch], ne, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-    }
+    if (owns && tid == 0) __hip_atomic_store(a.bp_ready + tile, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (dedup && !rank_first) dedup_rows();
 
     // 7. per-source counts for the source ranks that end in this tile
@@ -651,6 +638,46 @@ __device__ __forceinline__ void layout_block(const LayoutArgs &a, int tile, int 
             }
         }
     }
+
+    // 8. src_expert_off[s][e]: where the rows source rank s sends to expert
+    //    e start inside rank d(e)'s region, i.e. the expert's offset there
+    //    (the scan of step 4) plus the rows of e from earlier sources (the
+    //    expert key's prefix at boundary s). One tile has every boundary, its
+    //    copies taking the sources in turn; of several tiles the last one
+    //    (which holds the scan) reads the prefixes the boundary owners
+    //    published in step 6. Nothing on the dispatch path waits for it.
+    if (single) {
+        for (int e = tid; e < a.E; e += kTileTokens) {
+            const KeyView kv = key_view(masks, K, e);
+            const int eo = scan[e] - scan[rank_of(e, a.epr, a.epr_shift) * a.epr];
+            for (int s = replica; s < a.R; s += nrep)
+                a.src_expert_off[(size_t)s * a.E + e] = eo + count_before(kv, s * a.tpr, ntile);
+        }
+    } else if (last_tile && replica == 0) {
+        __syncthreads();  // every wave is past step 7 (scan and flags of this tile settled)
+        // boundary 0 is token 0 (prefix 0); this tile's own prefixes were
+        // stored and waited for before its step-6 barrier
+        for (int s = 1 + tid; s < a.R; s += kTileTokens) {
+            const int owner = (s * a.tpr) / kTileTokens;
+            if (owner == tile) continue;
+            uint32_t spins = 0;
+            while (__hip_atomic_load(a.bp_ready + owner, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != epoch) {
+                if (++spins > a.spin_limit) {
+                    atomicOr(&a.counters[kStatus], kStTimeout);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+        }
+        __threadfence();
+        __syncthreads();
+        for (int i = tid; i < a.R * a.E; i += kTileTokens) {
+            const int s = i / a.E, e = i - s * a.E;
+            const int pre =
+                s == 0 ? 0 : __hip_atomic_load(a.bp + (size_t)s * K + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            a.src_expert_off[i] = scan[e] - scan[rank_of(e, a.epr, a.epr_shift) * a.epr] + pre;
+        }
+    }
 }
 
 // Which tile (and replica) a block of a layout grid computes; -1: none.
@@ -676,15 +703,33 @@ __device__ __forceinline__ int layout_tile_of_block(const LayoutArgs &a, int b, 
     return tile;
 }
 
+// End of a layout or fused grid: the last block to finish re-arms the
+// workspace (ticket, done counter, next epoch). Every block has read the
+// epoch by then, so no block of this grid can tag its states with the next
+// call's epoch, even when a bounded wait gave up.
+__device__ __forceinline__ void rearm_workspace(const LayoutArgs &la) {
+    __syncthreads();
+    if (threadIdx.x == 0 && atomicAdd(&la.counters[kDone], 1u) == gridDim.x - 1) {
+        const uint32_t epoch = __hip_atomic_load(&la.counters[kEpoch], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        uint32_t ne = (epoch + 1u) & ((1u << 30) - 1u);
+        if (ne == 0) ne = 1;
+        __hip_atomic_store(&la.counters[kTicket], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&la.counters[kDone], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&la.counters[kEpoch], ne, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
 template <int KMAX>
 __global__ __launch_bounds__(kTileTokens) void k_layout(LayoutArgs a) {
     int replica, nrep;
     const int tile = layout_tile_of_block(a, (int)blockIdx.x, (int)gridDim.x, &replica, &nrep);
-    if (tile < 0) return;  // uniform over the block
-    int raw[KMAX];
-    load_slots<KMAX>(a, tile * kTileTokens + (int)threadIdx.x, raw);
-    const uint32_t epoch = load_epoch(a);  // (left in flight past the slots)
-    layout_block<KMAX>(a, tile, replica, nrep, kLayoutAlone, raw, epoch);
+    if (tile >= 0) {  // uniform over the block
+        int raw[KMAX];
+        load_slots<KMAX>(a, tile * kTileTokens + (int)threadIdx.x, raw);
+        const uint32_t epoch = load_epoch(a);  // (left in flight past the slots)
+        layout_block<KMAX>(a, tile, replica, nrep, kLayoutAlone, raw, epoch);
+    }
+    rearm_workspace(a);
 }
 
 // ---------------------------------------------------------------------------
@@ -1285,20 +1330,6 @@ __device__ __forceinline__ LayoutWait make_wait(const LayoutArgs &la, uint32_t e
     return lw;
 }
 
-// End of a fused grid: the last block to finish re-arms the workspace
-// (every block has read the epoch by then).
-__device__ __forceinline__ void fused_rearm(const LayoutArgs &la) {
-    __syncthreads();
-    if (threadIdx.x == 0 && atomicAdd(&la.counters[kDone], 1u) == gridDim.x - 1) {
-        const uint32_t epoch = __hip_atomic_load(&la.counters[kEpoch], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        uint32_t ne = (epoch + 1u) & ((1u << 30) - 1u);
-        if (ne == 0) ne = 1;
-        __hip_atomic_store(&la.counters[kTicket], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&la.counters[kDone], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&la.counters[kEpoch], ne, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-}
-
 // Layout and forward dispatch in one grid: blocks [0, lgrid) compute the
 // layout (the tiles, or the replicas of one tile), the rest are dispatch
 // waves that load and quantize their rows first and wait for the layout only
@@ -1350,7 +1381,7 @@ __global__ __launch_bounds__(kTileTokens) void k_layout_dispatch(LayoutArgs la, 
         fused_dispatch_block<FP8, kWavesPerBlock, MODE>(da, make_wait(la, epoch, tpb, kTotals), b - lgrid,
                                                         items - extra);
     }
-    fused_rearm(la);
+    rearm_workspace(la);
 }
 
 // ---------------------------------------------------------------------------

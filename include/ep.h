@@ -95,8 +95,9 @@ typedef struct {
     int32_t *recv_cnt;        /* [E] rows expert e receives */
     int32_t *expert_off;      /* [E] first row of expert e inside its rank's region */
     int32_t *rank_rows;       /* [R] rows rank d receives (may exceed cap_rows: see EP_ST_CAPACITY) */
-    int32_t *src_expert_off;  /* [R][E] rows of expert e from source ranks < s: where source s's rows start
-                                 inside e's rows (absolute row: d*cap_rows + expert_off[e] + this) */
+    int32_t *src_expert_off;  /* [R][E] where the rows source rank s sends to expert e start inside rank
+                                 d(e)'s region: expert_off[e] + rows of e from source ranks < s (absolute
+                                 rows d*cap_rows + this + [0, cnt_se[s][e])) */
     int32_t *rank_in_expert;  /* [T][k] number of earlier tokens routed to the same expert, -1 if the slot is dropped */
     uint8_t *is_token_in_rank;/* [T][R] 1 if token t has an expert on rank d */
     /* Rank-deduplicated exchange (optional: both NULL, or both set). The
