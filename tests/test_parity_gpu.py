@@ -100,69 +100,78 @@ def test_backward_parity_small():
 
 # ---------------------------------------------------------------------------
 # full-size configs in the launch configuration the bench times: the layout
-# and handle are compared entirely, rows and sums on sampled tokens
+# and handle are compared entirely, then every row and every token in chunks
 # ---------------------------------------------------------------------------
 
-def sample_tokens(T, n=256, seed=0):
-    rng = np.random.default_rng(seed)
-    return np.unique(np.concatenate([[0, 1, T // 2, T - 2, T - 1], rng.choice(T, min(n, T), replace=False)]))
+def chunk_rows(pos, toks):
+    """The receive rows a chunk of tokens owns (sorted) and the chunk's
+    positions renumbered into them (-1 kept)."""
+    sub = pos[toks]
+    need = used_rows(sub)
+    remap = np.full(int(need.max(initial=-1)) + 1, -1, np.int64)
+    remap[need] = np.arange(need.size)
+    pos_c = np.where(sub >= 0, remap[np.maximum(sub, 0)], -1).astype(np.int32)
+    return need, pos_c
 
 
-def sampled_checks(cfg, wl, g, pos, use_fp8, with_backward):
+def chunked_checks(cfg, wl, g, pos, use_fp8, with_backward, chunk=1024):
+    """Every token of the workload, a chunk at a time: its dispatch rows
+    (codes and scales, or bf16 copies, and weights), its combined bf16 row
+    and fp32 sums, and with the backward pair its combine_backward rows and
+    dispatch_backward row. A chunk is a complete sub-problem (a row and a
+    combined token depend only on their own token's inputs), so the oracle
+    runs on the chunk's tokens with its positions renumbered into the rows
+    the chunk owns; the chunks together cover every kept row."""
     orc = oracle.default()
     T, H = cfg.T, cfg.H
-    toks = sample_tokens(T)
-    # dispatch rows of sampled tokens: the oracle quantizes (or copies) one token at a time
-    for t in toks:
-        rows = pos[t][pos[t] >= 0]
-        if rows.size == 0:
-            continue
-        idx = torch.from_numpy(rows.astype(np.int64)).cuda()
-        if use_fp8:
-            q, s = orc.quantize_token(wl.x[t])
-            got = g.recv_x.index_select(0, idx).cpu().numpy()
-            assert np.all(got == q[None, :]), f"fp8 row of token {t} differs"
-            gs = g.recv_scales.index_select(0, idx).cpu().numpy()
-            assert np.all(gs.view(np.uint32) == s.view(np.uint32)[None, :])
-        else:
-            got = host_u16(g.recv_x.index_select(0, idx))
-            assert np.all(got == wl.x[t][None, :]), f"bf16 row of token {t} differs"
-        gw = g.recv_w.index_select(0, idx).cpu().numpy()
-        assert np.array_equal(gw, wl.topk_w[t][pos[t] >= 0])
-
-    # combine of sampled tokens: gather the rows they read, remap their positions
     n = cfg.R * g.buf.cap_rows
     eo = device_normal_bf16((n, H), seed=11)
-    sub_pos = pos[toks]
-    need = used_rows(sub_pos)
-    remap = np.full(n, -1, np.int64)
-    remap[need] = np.arange(need.size)
-    pos_c = np.where(sub_pos >= 0, remap[np.maximum(sub_pos, 0)], -1).astype(np.int32)
-    eo_sub = host_u16(eo.index_select(0, torch.from_numpy(need.astype(np.int64)).cuda()))
-    y_o = orc.combine(eo_sub, pos_c, wl.topk_w[toks])
     y = g.buf.combine(eo, g.handle, g.w)
-    yt = host_u16(y.index_select(0, torch.from_numpy(toks.astype(np.int64)).cuda()))
-    assert compare_bf16(yt, y_o, "combine (sampled)") == 1.0
+    acc = g.buf.combine_f32(eo, g.handle, g.w)
     if with_backward:
         gy = device_normal_bf16((T, H), seed=12)
         grows = g.buf.combine_backward(gy, g.handle)
-        gy_h = host_u16(gy.index_select(0, torch.from_numpy(toks.astype(np.int64)).cuda()))
-        for i, t in enumerate(toks):
-            rows = pos[t][pos[t] >= 0]
-            got = host_u16(grows.index_select(0, torch.from_numpy(rows.astype(np.int64)).cuda()))
-            assert np.all(got == gy_h[i][None, :]), f"combine_backward row of token {t}"
         G = device_normal_bf16((n, H), seed=13)
         gx = g.buf.dispatch_backward(G, g.handle, g.w)
-        G_sub = host_u16(G.index_select(0, torch.from_numpy(need.astype(np.int64)).cuda()))
-        gx_o = orc.dispatch_backward(G_sub, pos_c, wl.topk_w[toks])
-        gxt = host_u16(gx.index_select(0, torch.from_numpy(toks.astype(np.int64)).cuda()))
-        assert compare_bf16(gxt, gx_o, "dispatch_backward (sampled)") == 1.0
+    assert g.buf.status() == 0
+    covered = 0
+    for t0 in range(0, T, chunk):
+        toks = np.arange(t0, min(t0 + chunk, T))
+        tk = torch.from_numpy(toks).cuda()
+        need, pos_c = chunk_rows(pos, toks)
+        covered += need.size
+        idx = torch.from_numpy(need.astype(np.int64)).cuda()
+        w_c = wl.topk_w[toks]
+        rx_o, rs_o, rw_o = orc.dispatch(wl.x[toks], w_c, pos_c, need.size, use_fp8)
+        if use_fp8:
+            got = g.recv_x.index_select(0, idx).cpu().numpy()
+            assert np.array_equal(got, rx_o), f"fp8 rows of tokens {t0}.. differ"
+            gs = g.recv_scales.index_select(0, idx).cpu().numpy()
+            assert np.array_equal(gs.view(np.uint32), rs_o.view(np.uint32)), f"scales of tokens {t0}.. differ"
+        else:
+            assert np.array_equal(host_u16(g.recv_x.index_select(0, idx)), rx_o), f"bf16 rows of tokens {t0}.."
+        gw = g.recv_w.index_select(0, idx).cpu().numpy()
+        assert np.array_equal(gw.view(np.uint32), rw_o.view(np.uint32)), f"recv_w of tokens {t0}.."
+        eo_c = host_u16(eo.index_select(0, idx))
+        y_o, acc_o = orc.combine(eo_c, pos_c, w_c, return_acc=True)
+        assert compare_bf16(host_u16(y.index_select(0, tk)), y_o, "combine") == 1.0
+        acc_c = acc.index_select(0, tk).cpu().numpy()
+        assert f32_rel_diff(acc_c, acc_o) <= 1e-6
+        assert np.array_equal(acc_c.view(np.uint32), acc_o.view(np.uint32)), f"fp32 sums of tokens {t0}.."
+        if with_backward:
+            grows_o = orc.combine_backward(host_u16(gy.index_select(0, tk)), pos_c, need.size)
+            assert np.array_equal(host_u16(grows.index_select(0, idx)), grows_o), f"combine_backward {t0}.."
+            gx_o = orc.dispatch_backward(host_u16(G.index_select(0, idx)), pos_c, w_c)
+            assert compare_bf16(host_u16(gx.index_select(0, tk)), gx_o, "dispatch_backward") == 1.0
+        print(f"  tokens {t0}..{toks[-1]}: {need.size} rows exact", flush=True)
+    assert covered == int((pos >= 0).sum())
 
 
 @pytest.mark.parametrize("fused", [False, True], ids=["two_calls", "fused"])
 @pytest.mark.parametrize("name", ["prefill", "large"])
-def test_full_size_sampled(name, fused):
+def test_full_size(name, fused):
     cfg = CONFIGS[name]
+    print(f"full-size parity: {name} T={cfg.T} H={cfg.H} fused={fused}", flush=True)
     wl = make_workload(cfg, seed=0)
     orc = oracle.default()
     L = orc.layout(wl.topk_idx, cfg.E, cfg.R, 1 << 30)
@@ -173,7 +182,11 @@ def test_full_size_sampled(name, fused):
     assert g.status == L.status == 0
     compare_layout(g, L)
     compare_handle(g, pos, src)
-    sampled_checks(cfg, wl, g, pos, cfg.use_fp8, with_backward=cfg.backward or name == "prefill")
+    chunked_checks(cfg, wl, g, pos, cfg.use_fp8, with_backward=cfg.backward or name == "prefill")
+    g.buf.close()
+    del g
+    gc.collect()
+    torch.cuda.empty_cache()
 
 
 # ---------------------------------------------------------------------------
