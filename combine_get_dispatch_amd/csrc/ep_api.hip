@@ -18,9 +18,9 @@ struct ep_ctx {
     void *ws;
     size_t ws_bytes;
     uint32_t *counters;
+    uint32_t *status;  // where the kernels OR their status bits (the workspace's status word)
     uint64_t *tile_state;
-    int32_t *bp;
-    uint32_t *bp_ready;
+    uint64_t *bp;
     uint32_t *rank_ready;
     uint32_t spin_limit;
     bool debug;
@@ -45,7 +45,8 @@ constexpr int kCombineTargetWaves = 1 << 30;  // i.e. one pass per wave
 // resident blocks; the low-latency kernel and the forward dispatch gain
 // nothing from more waves.)
 constexpr int kBackwardTargetWaves = 1 << 30;
-constexpr int kFusedMaxTiles = 16;             // layout tiles up to which one grid does layout + dispatch
+constexpr int kFusedMaxTiles = 16;
+constexpr uint32_t kDefaultSpinLimit = 1u << 20;  // polls of a bounded wait before EP_ST_TIMEOUT             // layout tiles up to which one grid does layout + dispatch
 constexpr int kMaxPassPerWave = 8;   // must match ep_kernels.hip
 
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -70,10 +71,10 @@ int num_tiles_of(const ep_config &c) {
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// workspace: counters | tile states | boundary prefixes | boundary-ready
-// flags | rank-ready flags (one per layout block of a fused launch)
+// workspace: counters | tile states | boundary prefixes (epoch-tagged) |
+// rank-ready flags (one per layout block of a fused launch)
 struct WorkspaceLayout {
-    size_t state, bp, bp_ready, rank_ready, total;
+    size_t state, bp, rank_ready, total;
 };
 
 WorkspaceLayout workspace_layout(const ep_config &c) {
@@ -85,9 +86,7 @@ WorkspaceLayout workspace_layout(const ep_config &c) {
     w.state = off;
     off = round_up(off + tiles * keys * sizeof(uint64_t), 256);
     w.bp = off;
-    off = round_up(off + ((size_t)c.num_ranks + 1) * keys * sizeof(int32_t), 256);
-    w.bp_ready = off;
-    off = round_up(off + tiles * sizeof(uint32_t), 256);
+    off = round_up(off + ((size_t)c.num_ranks + 1) * keys * sizeof(uint64_t), 256);
     w.rank_ready = off;
     off = round_up(off + blocks * sizeof(uint32_t), 256);
     w.total = off;
@@ -158,6 +157,7 @@ int combine_common(ep_ctx *ctx, const uint16_t *rows, const ep_handle *h, const 
     a.passes_per_wave = g.ppw;
     a.npass = g.npass;
     a.counters = ctx->counters;
+    a.status = ctx->status;
     if (ctx->debug)
         std::fprintf(stderr, "libep: %s T=%d k=%d H=%d waves=%d (%d/token, %d passes each)\n", name, a.T, a.k,
                      a.H, g.num_waves, g.wpt, g.ppw);
@@ -206,6 +206,7 @@ int fill_dispatch(ep_ctx *ctx, const uint16_t *x, const int32_t *topk, const flo
     a.passes_per_wave = g.ppw;
     a.npass = g.npass;
     a.counters = ctx->counters;
+    a.status = ctx->status;
     return EP_OK;
 }
 
@@ -263,9 +264,9 @@ int fill_layout(ep_ctx *ctx, const int32_t *topk_idx, const ep_layout *L, ep::La
     a.src_expert_off = L->src_expert_off;
     a.tile_state = ctx->tile_state;
     a.bp = ctx->bp;
-    a.bp_ready = ctx->bp_ready;
     a.rank_ready = ctx->rank_ready;
     a.counters = ctx->counters;
+    a.status = ctx->status;
     a.spin_limit = ctx->spin_limit;
     // the deduplicated outputs: both or neither (no tokens: rank_in_rank is empty)
     if (L->rank_in_rank && !L->token_rows) return EP_ERR_ARG;
@@ -316,6 +317,10 @@ int check_forward_dispatch(ep_ctx *ctx, const int32_t *topk_idx, const float *to
     handle->num_topk = c.num_topk;
     return EP_OK;
 }
+
+int dispatch_with_layout(ep_ctx *ctx, const uint16_t *x, const int32_t *topk_idx, const float *topk_weights,
+                         const ep_layout *L, int use_fp8, void *recv_x, float *recv_scales, float *recv_w,
+                         ep_handle *handle, ep_stream_t stream);
 
 }  // namespace
 
@@ -377,7 +382,7 @@ int ep_create(const ep_config *cfg, ep_ctx **out) {
     const char *dbg = std::getenv("EP_DEBUG");
     ctx->debug = dbg && dbg[0] && dbg[0] != '0';
     const char *spin = std::getenv("EP_SPIN_LIMIT");
-    ctx->spin_limit = spin ? (uint32_t)std::strtoul(spin, nullptr, 10) : (1u << 20);
+    ctx->spin_limit = spin ? (uint32_t)std::strtoul(spin, nullptr, 10) : kDefaultSpinLimit;
     if (hipGetDevice(&ctx->device) != hipSuccess ||
         hipDeviceGetAttribute(&ctx->cu_count, hipDeviceAttributeMultiprocessorCount, ctx->device) != hipSuccess) {
         delete ctx;
@@ -392,14 +397,13 @@ int ep_create(const ep_config *cfg, ep_ctx **out) {
     }
     char *base = static_cast<char *>(ctx->ws);
     ctx->counters = reinterpret_cast<uint32_t *>(base);
+    ctx->status = ctx->counters + ep::kStatus;
     ctx->tile_state = reinterpret_cast<uint64_t *>(base + wl.state);
-    ctx->bp = reinterpret_cast<int32_t *>(base + wl.bp);
-    ctx->bp_ready = reinterpret_cast<uint32_t *>(base + wl.bp_ready);
+    ctx->bp = reinterpret_cast<uint64_t *>(base + wl.bp);
     ctx->rank_ready = reinterpret_cast<uint32_t *>(base + wl.rank_ready);
-    uint32_t init[ep::kNumCounters] = {0};
-    init[ep::kEpoch] = 1;  // tile states start at epoch 0 = "not published"
+    // all zero is the workspace's start: counters, and states and flags of
+    // epoch 0, which no call uses
     int r = hip_fail(hipMemset(ctx->ws, 0, ctx->ws_bytes), "hipMemset");
-    if (!r) r = hip_fail(hipMemcpy(ctx->counters, init, sizeof init, hipMemcpyHostToDevice), "hipMemcpy");
     if (!r) r = hip_fail(hipDeviceSynchronize(), "hipDeviceSynchronize");
     if (r) {
         (void)hipFree(ctx->ws);
@@ -515,6 +519,17 @@ int ep_dispatch_dedup_with_layout(ep_ctx *ctx, const uint16_t *x, const int32_t 
 int ep_dispatch_with_layout(ep_ctx *ctx, const uint16_t *x, const int32_t *topk_idx, const float *topk_weights,
                             const ep_layout *L, int use_fp8, void *recv_x, float *recv_scales, float *recv_w,
                             ep_handle *handle, ep_stream_t stream) {
+    return dispatch_with_layout(ctx, x, topk_idx, topk_weights, L, use_fp8, recv_x, recv_scales, recv_w, handle,
+                                stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+int dispatch_with_layout(ep_ctx *ctx, const uint16_t *x, const int32_t *topk_idx, const float *topk_weights,
+                         const ep_layout *L, int use_fp8, void *recv_x, float *recv_scales, float *recv_w,
+                         ep_handle *handle, ep_stream_t stream) {
     if (L && (L->rank_in_rank || L->token_rows)) return EP_ERR_ARG;  // per-expert rows only
     ep::LayoutArgs la;
     if (int r = fill_layout(ctx, topk_idx, L, la)) return r;
@@ -538,6 +553,10 @@ int ep_dispatch_with_layout(ep_ctx *ctx, const uint16_t *x, const int32_t *topk_
                         "ep_dispatch_with_layout");
     return launch_fused(ctx, la, da, use_fp8 != 0, 1, g.num_waves, stream, "ep_dispatch_with_layout");
 }
+
+}  // namespace
+
+extern "C" {
 
 int ep_combine(ep_ctx *ctx, const uint16_t *expert_out, const ep_handle *handle, const float *weights,
                uint16_t *combined_x, ep_stream_t stream) {
@@ -574,6 +593,12 @@ int ep_get_status(ep_ctx *ctx, ep_stream_t stream, uint32_t *status) {
     if (r) return r;
     const uint32_t zero = 0;
     return hip_fail(hipMemcpy(ctx->counters + ep::kStatus, &zero, sizeof zero, hipMemcpyHostToDevice), "hipMemcpy");
+}
+
+int ep_set_spin_limit(ep_ctx *ctx, uint32_t polls) {
+    if (!ctx) return EP_ERR_ARG;
+    ctx->spin_limit = polls ? polls : kDefaultSpinLimit;
+    return EP_OK;
 }
 
 int ep_set_cu_budget(ep_ctx *ctx, int num_cus) {

@@ -23,7 +23,9 @@ constexpr int kMaxTopk = 32;
 constexpr int kMaxRanks = 64;
 constexpr int kMaxExperts = 1024;
 
-// ctx workspace counters (uint32 each)
+// workspace counters (uint32 each). All zero is a valid start: the epoch
+// counter holds the current epoch minus one. kStatus is the context's status
+// word (kernels OR their status bits into the word `status` points at).
 enum Counter { kTicket = 0, kDone = 1, kEpoch = 2, kStatus = 3, kTotalsReady = 4, kNumCounters = 16 };
 
 struct LayoutArgs {
@@ -36,10 +38,10 @@ struct LayoutArgs {
     uint8_t *itr;
     int32_t *cnt_se, *cnt_sd, *recv_cnt, *expert_off, *rank_rows, *src_expert_off;
     uint64_t *tile_state;  // [num_tiles][E+R]
-    int32_t *bp;           // [R+1][E+R] prefixes at source-rank boundaries
-    uint32_t *bp_ready;    // [num_tiles] epoch once a tile's boundary prefixes are written
+    uint64_t *bp;          // [R+1][E+R] prefixes at source-rank boundaries, tagged (epoch << 32 | prefix)
     uint32_t *rank_ready;  // [layout blocks] epoch once a block's ranks are written (fused launch)
     uint32_t *counters;
+    uint32_t *status;  // sticky EP_ST_* bits
     uint32_t spin_limit;
     int32_t *rank_in_rank;  // [T][k] or NULL: the deduplicated exchange's rows (leader slots)
     int32_t *token_rows;    // [R] or NULL
@@ -63,6 +65,7 @@ struct DispatchArgs {
     int64_t cap_rows, num_rows;  // num_rows = R * cap_rows
     int waves_per_token, passes_per_wave, npass;
     uint32_t *counters;
+    uint32_t *status;            // sticky EP_ST_* bits
 };
 
 struct CombineArgs {
@@ -74,6 +77,7 @@ struct CombineArgs {
     int64_t num_rows;      // rows of `rows`; positions outside are skipped
     int waves_per_token, passes_per_wave, npass;
     uint32_t *counters;
+    uint32_t *status;      // sticky EP_ST_* bits
 };
 
 hipError_t launch_layout(const LayoutArgs &a, hipStream_t s);

@@ -199,8 +199,12 @@ __device__ __forceinline__ void load_slots(const LayoutArgs &a, int t, int (&raw
         if (t >= a.T || j >= a.k) raw[j] = -1;
 }
 
+// The call's epoch: the epoch counter plus one, so that a workspace filled
+// with zeros is a valid start (no state or flag carries epoch 0). Epochs run
+// through 1 .. 2^30 - 1 (30 bits of a look-back state word).
+constexpr uint32_t kEpochPeriod = (1u << 30) - 1u;
 __device__ __forceinline__ uint32_t load_epoch(const LayoutArgs &a) {
-    return __hip_atomic_load(&a.counters[kEpoch], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return __hip_atomic_load(&a.counters[kEpoch], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
 }
 
 // One key's count in each wave of the tile and in the tile (LDS), published
@@ -232,6 +236,12 @@ struct TileView {
     bool single;
     int replica, nrep, t0, ntile, first_lo, first_hi;
 };
+
+// A boundary prefix as stored for other tiles: the call's epoch in the high
+// word, so that a reader can tell this call's value from an older one.
+__device__ __forceinline__ uint64_t tag_prefix(uint32_t epoch, int v) {
+    return ((uint64_t)epoch << 32) | (uint32_t)v;
+}
 
 // Decoupled look-back of one key, a window of predecessors per round trip:
 // add counts from the nearest predecessor back to the first inclusive
@@ -275,7 +285,7 @@ __device__ __forceinline__ void lookback_key(const TileView &v, int key) {
             hi -= consumed;
             if (stall) {
                 if (++spins > a.spin_limit) {
-                    atomicOr(&a.counters[kStatus], kStTimeout);
+                    atomicOr(a.status, kStTimeout);
                     break;
                 }
                 __builtin_amdgcn_s_sleep(1);
@@ -301,7 +311,37 @@ __device__ __forceinline__ void lookback_key(const TileView &v, int key) {
         }
     } else {
         for (int s = v.first_lo; s < v.first_hi; ++s)
-            store_agent(a.bp + (size_t)s * K + key, sum + count_before(kv, s * a.tpr - v.t0, v.ntile));
+            __hip_atomic_store(a.bp + (size_t)s * K + key,
+                               tag_prefix(v.epoch, sum + count_before(kv, s * a.tpr - v.t0, v.ntile)),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// Boundary prefixes read by other tiles of the same call: B words of bp per
+// thread (entry u at offset at[u] when use[u]), all loads issued before the
+// first wait. A word tagged with an older epoch is not yet written for this
+// call and is read again (bounded, EP_ST_TIMEOUT); unused entries give 0.
+template <int B>
+__device__ __forceinline__ void load_prefixes(const LayoutArgs &a, const size_t (&at)[B], const bool (&use)[B],
+                                              uint32_t epoch, int (&out)[B]) {
+    uint64_t w[B];
+#pragma unroll
+    for (int u = 0; u < B; ++u)
+        w[u] = use[u] ? __hip_atomic_load(a.bp + at[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                      : tag_prefix(epoch, 0);
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+        uint32_t spins = 0;
+        while ((uint32_t)(w[u] >> 32) != epoch) {
+            if (++spins > a.spin_limit) {
+                atomicOr(a.status, kStTimeout);
+                w[u] = tag_prefix(epoch, 0);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+            w[u] = __hip_atomic_load(a.bp + at[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        out[u] = (int32_t)(uint32_t)w[u];
     }
 }
 
@@ -341,7 +381,6 @@ __device__ __forceinline__ void layout_block(const LayoutArgs &a, int tile, int 
         last_hi = min((t0 + kTileTokens) / a.tpr, a.R);
         if (last_tile) last_hi = a.R;
     }
-    const bool owns = first_hi > first_lo;  // boundary prefixes to publish (several tiles)
 
     // each wave clears its own masks (LDS operations of a wave are ordered):
     // no barrier before the atomics
@@ -387,7 +426,7 @@ __device__ __forceinline__ void layout_block(const LayoutArgs &a, int tile, int 
     // tokens whose per-token outputs this block writes (all of them unless replicated)
     const int tok_chunk = (ntile + nrep - 1) / nrep;
     const bool my_token = t < a.T && tid >= replica * tok_chunk && tid < (replica + 1) * tok_chunk;
-    if (st && replica == 0) atomicOr(&a.counters[kStatus], st);
+    if (st && replica == 0) atomicOr(a.status, st);
     __syncthreads();
 
     const TileView tv{a, masks, agg, excl, K, tile, epoch, single, replica, nrep, t0, ntile, first_lo, first_hi};
@@ -455,7 +494,7 @@ __device__ __forceinline__ void layout_block(const LayoutArgs &a, int tile, int 
             for (int d = tid; d < a.R; d += kTileTokens) {
                 const int rows = excl[a.E + d] + agg[a.E + d];
                 a.token_rows[d] = rows;
-                if ((int64_t)rows > a.cap_rows) atomicOr(&a.counters[kStatus], kStCap);
+                if ((int64_t)rows > a.cap_rows) atomicOr(a.status, kStCap);
             }
         if (fused) {
             wait_own_stores();
@@ -514,10 +553,11 @@ __device__ __forceinline__ void layout_block(const LayoutArgs &a, int tile, int 
             for (int d = tid; d < a.R; d += kTileTokens) {
                 const int rows = scan[(d + 1) * a.epr] - scan[d * a.epr];
                 a.rank_rows[d] = rows;
-                if (!a.token_rows && (int64_t)rows > a.cap_rows) atomicOr(&a.counters[kStatus], kStCap);
+                if (!a.token_rows && (int64_t)rows > a.cap_rows) atomicOr(a.status, kStCap);
             }
-            if (fused) {
-                // expert offsets are readable by the dispatch waves from here on
+            if (fused || !single) {
+                // expert offsets are readable by the dispatch waves and the
+                // src_expert_off block (several tiles) from here on
                 wait_own_stores();
                 __syncthreads();
                 if (tid == 0)
@@ -589,41 +629,34 @@ __device__ __forceinline__ void layout_block(const LayoutArgs &a, int tile, int 
                                __HIP_MEMORY_SCOPE_AGENT);
     }
 
-    // 6. the rank keys (unless done first, see above), then the boundary
-    //    prefixes this tile owns, published once both kinds of keys have
-    //    stored theirs (each thread waits for its own agent-scope stores
-    //    before the barrier that precedes the flag). The workspace is re-armed
-    //    by the last block of the grid to finish.
+    // 6. the rank keys (unless done first, see above); their look-back also
+    //    stores this tile's boundary prefixes of the rank keys. The workspace
+    //    is re-armed by the last block of the grid to finish.
     if (!rank_first) rank_keys();
-    if (owns) wait_own_stores();
     __syncthreads();
-    if (owns && tid == 0) __hip_atomic_store(a.bp_ready + tile, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (dedup && !rank_first) dedup_rows();
 
     // 7. per-source counts for the source ranks that end in this tile
     //    (source s = tokens [s*T/R, (s+1)*T/R)); a start boundary owned by an
-    //    earlier tile is read back once that tile has published its prefixes
+    //    earlier tile is read back from the prefixes that tile stored
     if (!single && last_hi > last_lo) {
         const bool remote = last_lo * a.tpr < t0;  // only the first such source can start earlier
         int32_t *remote_lo = wpre;                 // [K] its start prefixes (wpre is free after step 5)
         if (remote) {
             __syncthreads();  // every wave is past step 5
-            if (tid == 0) {
-                const int owner = (last_lo * a.tpr) / kTileTokens;
-                uint32_t spins = 0;
-                while (__hip_atomic_load(a.bp_ready + owner, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != epoch) {
-                    if (++spins > a.spin_limit) {
-                        atomicOr(&a.counters[kStatus], kStTimeout);
-                        break;
-                    }
-                    __builtin_amdgcn_s_sleep(1);
-                }
-                __threadfence();
+            constexpr int kKeysPerThread = (kMaxExperts + kMaxRanks + kTileTokens - 1) / kTileTokens;
+            size_t at[kKeysPerThread];
+            bool use[kKeysPerThread];
+            int pre[kKeysPerThread];
+#pragma unroll
+            for (int u = 0; u < kKeysPerThread; ++u) {
+                at[u] = (size_t)last_lo * K + tid + u * kTileTokens;
+                use[u] = tid + u * kTileTokens < K;
             }
-            __syncthreads();
-            for (int key = tid; key < K; key += kTileTokens)
-                remote_lo[key] = __hip_atomic_load(a.bp + (size_t)last_lo * K + key, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT);
+            load_prefixes<kKeysPerThread>(a, at, use, epoch, pre);
+#pragma unroll
+            for (int u = 0; u < kKeysPerThread; ++u)
+                if (use[u]) remote_lo[tid + u * kTileTokens] = pre[u];
         }
         for (int key = tid; key < K; key += kTileTokens) {
             const KeyView kv = key_view(masks, K, key);
@@ -641,11 +674,10 @@ __device__ __forceinline__ void layout_block(const LayoutArgs &a, int tile, int 
 
     // 8. src_expert_off[s][e]: where the rows source rank s sends to expert
     //    e start inside rank d(e)'s region, i.e. the expert's offset there
-    //    (the scan of step 4) plus the rows of e from earlier sources (the
-    //    expert key's prefix at boundary s). One tile has every boundary, its
-    //    copies taking the sources in turn; of several tiles the last one
-    //    (which holds the scan) reads the prefixes the boundary owners
-    //    published in step 6. Nothing on the dispatch path waits for it.
+    //    (the scan of step 4) plus the rows of e from earlier sources. One
+    //    tile has every boundary, its copies taking the sources in turn; of
+    //    several tiles the last one writes it once its grid's other work is
+    //    done (gather_src_expert_off).
     if (single) {
         for (int e = tid; e < a.E; e += kTileTokens) {
             const KeyView kv = key_view(masks, K, e);
@@ -653,36 +685,54 @@ __device__ __forceinline__ void layout_block(const LayoutArgs &a, int tile, int 
             for (int s = replica; s < a.R; s += nrep)
                 a.src_expert_off[(size_t)s * a.E + e] = eo + count_before(kv, s * a.tpr, ntile);
         }
-    } else if (last_tile && replica == 0) {
-        __syncthreads();  // every wave is past step 7 (scan and flags of this tile settled)
-        // boundary 0 is token 0 (prefix 0); this tile's own prefixes were
-        // stored and waited for before its step-6 barrier
-        for (int s = 1 + tid; s < a.R; s += kTileTokens) {
-            const int owner = (s * a.tpr) / kTileTokens;
-            if (owner == tile) continue;
-            uint32_t spins = 0;
-            while (__hip_atomic_load(a.bp_ready + owner, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != epoch) {
-                if (++spins > a.spin_limit) {
-                    atomicOr(&a.counters[kStatus], kStTimeout);
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(1);
+    }
+}
+
+// src_expert_off of several tiles, by one extra block of the layout grid
+// that follows the tiles in launch order (so everything it waits for is
+// already running): once the last tile has published the expert offsets
+// (the totals flag), the expert key's prefix at boundary s, which the
+// boundary's owner stored in its look-back, plus the expert's offset in its
+// rank. It overlaps the last tile's remaining work, and nothing on the
+// dispatch path waits for it. Each thread takes experts tid, tid + 256, ...
+// and loads sixteen boundaries' prefixes at a time before storing.
+__device__ __forceinline__ void gather_src_expert_off(const LayoutArgs &a, uint32_t epoch) {
+    const int tid = threadIdx.x, K = a.E + a.R;
+    if (tid == 0) {
+        uint32_t spins = 0;
+        while (__hip_atomic_load(&a.counters[kTotalsReady], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != epoch) {
+            if (++spins > a.spin_limit) {
+                atomicOr(a.status, kStTimeout);
+                break;
             }
+            __builtin_amdgcn_s_sleep(2);
         }
-        __threadfence();
-        __syncthreads();
-        for (int i = tid; i < a.R * a.E; i += kTileTokens) {
-            const int s = i / a.E, e = i - s * a.E;
-            const int pre =
-                s == 0 ? 0 : __hip_atomic_load(a.bp + (size_t)s * K + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            a.src_expert_off[i] = scan[e] - scan[rank_of(e, a.epr, a.epr_shift) * a.epr] + pre;
+    }
+    __syncthreads();
+    constexpr int kBatch = 16;
+    for (int e = tid; e < a.E; e += kTileTokens) {
+        const int eo = __hip_atomic_load(a.expert_off + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int s0 = 0; s0 < a.R; s0 += kBatch) {
+            size_t at[kBatch];
+            bool use[kBatch];
+            int pre[kBatch];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                at[u] = (size_t)(s0 + u) * K + e;
+                use[u] = s0 + u < a.R && s0 + u > 0;  // boundary 0 is token 0: prefix 0
+            }
+            load_prefixes<kBatch>(a, at, use, epoch, pre);
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u)
+                if (s0 + u < a.R) a.src_expert_off[(size_t)(s0 + u) * a.E + e] = eo + pre[u];
         }
     }
 }
 
-// Which tile (and replica) a block of a layout grid computes; -1: none.
-// Grids larger than the co-resident limit number tiles by start order (a
-// ticket), so that every predecessor is already running.
+// Which tile (and replica) a block of a layout grid computes; num_tiles: the
+// src_expert_off block that follows several tiles; -1: none. Grids larger
+// than the co-resident limit number tiles by start order (a ticket), so that
+// every predecessor is already running.
 __device__ __forceinline__ int layout_tile_of_block(const LayoutArgs &a, int b, int nblocks, int *replica, int *nrep) {
     __shared__ int s_tile;
     *replica = 0;
@@ -696,8 +746,8 @@ __device__ __forceinline__ int layout_tile_of_block(const LayoutArgs &a, int b, 
     if (threadIdx.x == 0) s_tile = (int)atomicAdd(&a.counters[kTicket], 1u);
     __syncthreads();
     const int tile = s_tile;
-    if (tile >= a.num_tiles) {  // workspace not re-armed (an earlier call did not finish)
-        if (threadIdx.x == 0) atomicOr(&a.counters[kStatus], kStTimeout);
+    if (tile > a.num_tiles) {  // workspace not re-armed (an earlier call did not finish)
+        if (threadIdx.x == 0) atomicOr(a.status, kStTimeout);
         return -1;
     }
     return tile;
@@ -710,12 +760,11 @@ __device__ __forceinline__ int layout_tile_of_block(const LayoutArgs &a, int b, 
 __device__ __forceinline__ void rearm_workspace(const LayoutArgs &la) {
     __syncthreads();
     if (threadIdx.x == 0 && atomicAdd(&la.counters[kDone], 1u) == gridDim.x - 1) {
-        const uint32_t epoch = __hip_atomic_load(&la.counters[kEpoch], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        uint32_t ne = (epoch + 1u) & ((1u << 30) - 1u);
-        if (ne == 0) ne = 1;
+        const uint32_t c = __hip_atomic_load(&la.counters[kEpoch], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(&la.counters[kTicket], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(&la.counters[kDone], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&la.counters[kEpoch], ne, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&la.counters[kEpoch], (c + 1u) % kEpochPeriod, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -723,11 +772,13 @@ template <int KMAX>
 __global__ __launch_bounds__(kTileTokens) void k_layout(LayoutArgs a) {
     int replica, nrep;
     const int tile = layout_tile_of_block(a, (int)blockIdx.x, (int)gridDim.x, &replica, &nrep);
-    if (tile >= 0) {  // uniform over the block
+    if (tile >= 0 && tile < a.num_tiles) {  // uniform over the block
         int raw[KMAX];
         load_slots<KMAX>(a, tile * kTileTokens + (int)threadIdx.x, raw);
         const uint32_t epoch = load_epoch(a);  // (left in flight past the slots)
         layout_block<KMAX>(a, tile, replica, nrep, kLayoutAlone, raw, epoch);
+    } else if (tile == a.num_tiles) {
+        gather_src_expert_off(a, load_epoch(a));
     }
     rearm_workspace(a);
 }
@@ -888,7 +939,7 @@ __device__ __forceinline__ int slot_finish(const DispatchArgs &a, int t, int lan
         } else {
             p = s.e;
             if (p < -1 || p >= a.num_rows) {  // not a position this buffer holds
-                atomicOr(&a.counters[kStatus], kStBadHandle);
+                atomicOr(a.status, kStBadHandle);
                 p = -1;
             }
         }
@@ -1241,7 +1292,7 @@ __global__ __launch_bounds__(kTileTokens) void k_ll_dispatch(DispatchArgs da, in
         for (int j = 0; j < KMAX; ++j)
             if (j < da.k) slots[tid * da.k + j] = ev[j];
     }
-    if (st && bi == 0) atomicOr(&da.counters[kStatus], st);
+    if (st && bi == 0) atomicOr(da.status, st);
     __syncthreads();  // masks and slots complete
     if (bi == 0)
         for (int e = tid; e < da.E; e += kTileTokens) {
@@ -1323,7 +1374,7 @@ __device__ __forceinline__ LayoutWait make_wait(const LayoutArgs &la, uint32_t e
     LayoutWait lw;
     lw.rank_ready = la.rank_ready;
     lw.totals_ready = totals ? la.counters + kTotalsReady : nullptr;
-    lw.status = la.counters + kStatus;
+    lw.status = la.status;
     lw.epoch = epoch;
     lw.spin_limit = la.spin_limit;
     lw.tokens_per_block = max(tokens_per_block, 1);
@@ -1376,6 +1427,10 @@ __global__ __launch_bounds__(kTileTokens) void k_layout_dispatch(LayoutArgs la, 
             const int p = slot_finish<MODE>(da, t, lane, part, s, l);
             write_rows<FP8>(da, part, p, v, sc);
         }
+    } else if (la.num_tiles > 1 && b == (int)gridDim.x - 1) {
+        // the src_expert_off block, last in the grid (it starts once a slot
+        // frees; everything it waits for runs before it)
+        gather_src_expert_off(la, load_epoch(la));
     } else {
         const uint32_t epoch = load_epoch(la);
         fused_dispatch_block<FP8, kWavesPerBlock, MODE>(da, make_wait(la, epoch, tpb, kTotals), b - lgrid,
@@ -1403,7 +1458,7 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void k_combine(CombineArgs a) 
     if (lane < a.k) {
         p = a.pos[(size_t)t * a.k + lane];
         if (p < -1 || p >= a.num_rows) {  // not a position this buffer holds
-            atomicOr(&a.counters[kStatus], kStBadHandle);
+            atomicOr(a.status, kStBadHandle);
             p = -1;
         }
         if (a.w) wt = a.w[(size_t)t * a.k + lane];
@@ -1529,8 +1584,9 @@ __global__ __launch_bounds__(64) void k_cu_census(uint32_t *__restrict__ ids, in
 
 hipError_t launch_layout(const LayoutArgs &a, hipStream_t s) {
     const size_t lds = layout_lds_bytes(a.E + a.R);
-    // one tile: up to kLayoutReplicas copies, each writing a slice of the outputs
-    const int grid = a.num_tiles > 1 ? a.num_tiles : max(1, min(a.R, kLayoutReplicas));
+    // one tile: up to kLayoutReplicas copies, each writing a slice of the
+    // outputs; several: the tiles and the src_expert_off block
+    const int grid = a.num_tiles > 1 ? a.num_tiles + 1 : max(1, min(a.R, kLayoutReplicas));
     if (a.k <= 8)
         hipLaunchKernelGGL(k_layout<8>, dim3(grid), dim3(kTileTokens), lds, s, a);
     else
@@ -1578,7 +1634,8 @@ hipError_t launch_layout_dispatch(const LayoutArgs &la, const DispatchArgs &da, 
     const int full = lgrid + (num_waves + kWavesPerBlock - 1) / kWavesPerBlock;
     if (!la.use_ticket && resident_blocks > 0 && full > resident_blocks)
         extra = min(num_waves, min(lgrid, full - resident_blocks) * kWavesPerBlock);
-    const dim3 grid(lgrid + (num_waves - extra + kWavesPerBlock - 1) / kWavesPerBlock);
+    // (several tiles: one more block, last, writes src_expert_off)
+    const dim3 grid(lgrid + (num_waves - extra + kWavesPerBlock - 1) / kWavesPerBlock + (la.num_tiles > 1 ? 1 : 0));
     if (la.k <= 8) {
         if (fp8)
             launch_layout_dispatch_t<8, true>(la, da, mode, grid, lds, lgrid, extra, s);

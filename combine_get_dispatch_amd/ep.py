@@ -99,6 +99,7 @@ SIGNATURES = {
     "ep_stream_create_cus": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.POINTER(c_void_p)]),
     "ep_stream_destroy": (ctypes.c_int, [c_void_p]),
     "ep_set_cu_budget": (ctypes.c_int, [c_void_p, ctypes.c_int]),
+    "ep_set_spin_limit": (ctypes.c_int, [c_void_p, ctypes.c_uint32]),
     "ep_cu_census": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, c_void_p, c_void_p]),
 }
 
@@ -265,6 +266,10 @@ def ep_stream_create_cus(num_cus: int, exclude: bool = False) -> int:
 
 def ep_set_cu_budget(ctx: int, num_cus: int) -> None:
     _check(load().ep_set_cu_budget(ctx, num_cus), "ep_set_cu_budget")
+
+
+def ep_set_spin_limit(ctx: int, polls: int) -> None:
+    _check(load().ep_set_spin_limit(ctx, polls), "ep_set_spin_limit")
 
 
 def ep_stream_destroy(stream: int) -> None:
@@ -521,6 +526,10 @@ class Buffer:
         """The compute units the stream these calls run on may use (0 = all);
         see CuStream."""
         ep_set_cu_budget(self.ctx, num_cus)
+
+    def set_spin_limit(self, polls: int) -> None:
+        """Polls of a bounded wait before it gives up with EP_ST_TIMEOUT (0 = default)."""
+        ep_set_spin_limit(self.ctx, polls)
 
     def status(self) -> int:
         """Synchronize the current stream; return and clear the sticky status bits."""

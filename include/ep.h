@@ -280,6 +280,16 @@ int ep_dispatch_backward(ep_ctx *ctx, const uint16_t *grad_rows, const ep_handle
  * them. Returns EP_OK or EP_ERR_HIP. */
 int ep_get_status(ep_ctx *ctx, ep_stream_t stream, uint32_t *status);
 
+/* The pages say nothing of failure detection; this is the library's own.
+ * Every wait of one block on another (the layout's look-back, a fused
+ * grid's readiness flags) polls at most `polls` times (0: the default,
+ * 2^20; ep_create reads an initial value from the EP_SPIN_LIMIT environment
+ * variable) and then gives up, setting EP_ST_TIMEOUT; the grid still ends,
+ * and its workspace is re-armed for the next call on the context. Applies
+ * to calls made after it returns. Returns EP_OK, or EP_ERR_ARG for a NULL
+ * context. */
+int ep_set_spin_limit(ep_ctx *ctx, uint32_t polls);
+
 /* Compute-unit cap ([Notes] §2: the normal kernels can be held to a chosen
  * number of SMs so that the rest stay free for computation running beside
  * them). On this GPU the cap is a property of the stream: kernels launched on

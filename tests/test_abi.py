@@ -146,5 +146,6 @@ def test_new_entry_points_reject_null_without_gpu(lib):
     assert L.ep_dispatch_dedup_with_layout(None, None, None, None, None, 0, None, None, None, None, None,
                                            None) == ep.EP_ERR_ARG
     assert L.ep_set_cu_budget(None, 8) == ep.EP_ERR_ARG
+    assert L.ep_set_spin_limit(None, 1) == ep.EP_ERR_ARG
     assert L.ep_cu_census(0, 0, None, None) == ep.EP_OK  # nothing to launch
     assert L.ep_cu_census(16, 65, None, None) == ep.EP_ERR_ARG

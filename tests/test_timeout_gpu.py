@@ -59,3 +59,35 @@ def test_spin_limit_reports_timeout_then_fresh_context_is_exact(monkeypatch, ded
         pos_o, _ = orc.positions(topk, L2, E, R, cap)
         assert np.array_equal(host(L.rank_in_expert), L2.rank_in_expert)
     assert np.array_equal(host(h.pos), pos_o)
+
+
+def test_layout_timeout_then_same_context_is_exact():
+    """The two-call path beyond the fused grid's sixteen tiles: with a spin
+    limit of 1 the standalone layout's look-back gives up (EP_ST_TIMEOUT);
+    its grid still re-arms the workspace when its last block ends, so the
+    next call on the same context, with the default limit, is exact (no
+    tile of the first call can tag states with the second call's epoch)."""
+    T, k, E, R = 65536, 4, 64, 8  # 256 tiles
+    rng = np.random.default_rng(10)
+    topk = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32)
+    orc = oracle.default()
+    cap = int(orc.layout(topk, E, R, 1 << 30).rank_rows.max())
+    L_o = orc.layout(topk, E, R, cap)
+    buf = ep.Buffer(T, 8, k, E, R, cap)
+    td = dev(topk)
+    timed_out = False
+    # whether a wait gives up at one poll depends on timing: try a few times
+    for _ in range(8):
+        buf.set_spin_limit(1)
+        buf.get_dispatch_layout(td)
+        timed_out = bool(buf.status() & ep.EP_ST_TIMEOUT)
+        buf.set_spin_limit(0)
+        L = buf.get_dispatch_layout(td)
+        assert buf.status() == 0
+        for key in ("rank_in_expert", "src_expert_off", "cnt_se", "cnt_sd", "expert_off"):
+            assert np.array_equal(host(getattr(L, key)), getattr(L_o, key)), key
+        if timed_out:
+            break
+    buf.close()
+    if not timed_out:
+        pytest.skip("no wait gave up at one poll in 8 calls: the re-arm after a timeout was not exercised")
