@@ -5,6 +5,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 
 #include "ep.h"
@@ -322,6 +323,76 @@ int dispatch_with_layout(ep_ctx *ctx, const uint16_t *x, const int32_t *topk_idx
                          const ep_layout *L, int use_fp8, void *recv_x, float *recv_scales, float *recv_w,
                          ep_handle *handle, ep_stream_t stream);
 
+// ---------------------------------------------------------------------------
+// The workspace of ep_dispatch_with_layout_noalloc, for callers that cannot
+// allocate: a static device array (each GPU the library runs on holds its
+// own copy until the process ends). Zero at load, which is a valid workspace
+// start (see ep_internal.h). Its host-side name is not a device address:
+// host code uses only the address hipGetSymbolAddress returns for the
+// current device, taken once per device.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = (size_t)4 << 20;
+constexpr int kMaxDevices = 64;
+// Each part of the array has one fixed place whatever the call's sizes, so
+// that a word always holds the same kind of value (a flag an epoch, a
+// look-back state a tagged state): a call of one size never reads what a
+// call of another size stored (its boundary prefixes, say) as a ready flag.
+constexpr int kScratchMaxTiles = 4096;
+constexpr size_t kScratchRankReady = 256;  // after the counters: [layout blocks] flags
+constexpr size_t kScratchBp = kScratchRankReady + (size_t)kScratchMaxTiles * 4;  // [R+1][E+R] tagged prefixes
+constexpr size_t kScratchStates =
+    kScratchBp + ((size_t)(ep::kMaxRanks + 1) * (ep::kMaxExperts + ep::kMaxRanks) * 8 + 255) / 256 * 256;
+
+// Whether a config's layout fits the static workspace: its tiles' flags and
+// look-back states ([tiles][E+R] 8-byte words after the fixed parts).
+bool fits_scratch(const ep_config &c) {
+    const size_t tiles = (size_t)num_tiles_of(c), keys = (size_t)c.num_experts + c.num_ranks;
+    return tiles <= (size_t)kScratchMaxTiles && tiles * keys * 8 <= kScratchBytes - kScratchStates;
+}
+
+struct ScratchDevice {
+    void *ptr;                  // the array's address on this device (NULL until set up)
+    int cu_count;
+    int fused_per_cu[2][2][2];  // as ep_ctx::fused_per_cu
+    uint32_t spin_limit;
+    bool debug;
+};
+
+std::mutex g_scratch_mu;
+ScratchDevice g_scratch_dev[kMaxDevices];
+
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+
+// The static workspace on device `dev` (current), set up on its first use.
+int scratch_device(int dev, ScratchDevice **out) {
+    if (dev < 0 || dev >= kMaxDevices) return EP_ERR_ARG;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    ScratchDevice &d = g_scratch_dev[dev];
+    if (!d.ptr) {
+        void *p = nullptr;
+        if (int r = hip_fail(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress")) return r;
+        if (!p) return EP_ERR_HIP;
+        int cus = 0;
+        if (int r = hip_fail(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev),
+                             "hipDeviceGetAttribute"))
+            return r;
+        d.cu_count = cus;
+        for (auto &plane : d.fused_per_cu)
+            for (auto &row : plane) row[0] = row[1] = -1;
+        const char *spin = std::getenv("EP_SPIN_LIMIT");
+        d.spin_limit = spin ? (uint32_t)std::strtoul(spin, nullptr, 10) : kDefaultSpinLimit;
+        const char *dbg = std::getenv("EP_DEBUG");
+        d.debug = dbg && dbg[0] && dbg[0] != '0';
+        d.ptr = p;
+    }
+    *out = &d;
+    return EP_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -335,6 +406,7 @@ const char *ep_strerror(int code) {
         case EP_ERR_ALIGN: return "misaligned pointer (row arrays need 16-byte alignment)";
         case EP_ERR_HIP: return "HIP runtime error";
         case EP_ERR_NOMEM: return "out of device memory";
+        case EP_ERR_SCRATCH: return "workload needs more workspace than the static scratch (4 MiB) of the no-allocation call";
         default: return "unknown error";
     }
 }
@@ -521,6 +593,48 @@ int ep_dispatch_with_layout(ep_ctx *ctx, const uint16_t *x, const int32_t *topk_
                             ep_handle *handle, ep_stream_t stream) {
     return dispatch_with_layout(ctx, x, topk_idx, topk_weights, L, use_fp8, recv_x, recv_scales, recv_w, handle,
                                 stream);
+}
+
+int ep_dispatch_with_layout_noalloc(const ep_config *cfg, const uint16_t *x, const int32_t *topk_idx,
+                                    const float *topk_weights, const ep_layout *L, int use_fp8, void *recv_x,
+                                    float *recv_scales, float *recv_w, ep_handle *handle, uint32_t *status,
+                                    ep_stream_t stream) {
+    if (int r = validate_config(cfg)) return r;
+    if (!fits_scratch(*cfg)) return EP_ERR_SCRATCH;
+    if (!aligned(status, 4)) return EP_ERR_ALIGN;
+    int dev = -1;
+    if (int r = hip_fail(hipGetDevice(&dev), "hipGetDevice")) return r;
+    ScratchDevice *sd = nullptr;
+    if (int r = scratch_device(dev, &sd)) return r;
+    // a context on the stack over this device's static workspace
+    ep_ctx ctx{};
+    ctx.cfg = *cfg;
+    ctx.device = dev;
+    ctx.num_tiles = num_tiles_of(*cfg);
+    ctx.keys = cfg->num_experts + cfg->num_ranks;
+    ctx.ws = sd->ptr;
+    ctx.ws_bytes = kScratchBytes;
+    char *base = static_cast<char *>(sd->ptr);
+    ctx.counters = reinterpret_cast<uint32_t *>(base);
+    ctx.status = status ? status : ctx.counters + ep::kStatus;
+    ctx.tile_state = reinterpret_cast<uint64_t *>(base + kScratchStates);
+    ctx.bp = reinterpret_cast<uint64_t *>(base + kScratchBp);
+    ctx.rank_ready = reinterpret_cast<uint32_t *>(base + kScratchRankReady);
+    ctx.spin_limit = sd->spin_limit;
+    ctx.debug = sd->debug;
+    ctx.cu_count = sd->cu_count;
+    ctx.cu_budget = 0;
+    {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        std::memcpy(ctx.fused_per_cu, sd->fused_per_cu, sizeof ctx.fused_per_cu);
+    }
+    const int r = dispatch_with_layout(&ctx, x, topk_idx, topk_weights, L, use_fp8, recv_x, recv_scales, recv_w,
+                                       handle, stream);
+    {  // keep what the call learned of the fused kernel's occupancy
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        std::memcpy(sd->fused_per_cu, ctx.fused_per_cu, sizeof ctx.fused_per_cu);
+    }
+    return r;
 }
 
 }  // extern "C"

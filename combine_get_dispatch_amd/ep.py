@@ -21,6 +21,7 @@ EP_ERR_ARG = -1
 EP_ERR_ALIGN = -2
 EP_ERR_HIP = -3
 EP_ERR_NOMEM = -4
+EP_ERR_SCRATCH = -5
 
 EP_ST_BAD_EXPERT = 1
 EP_ST_DUP_EXPERT = 2
@@ -75,6 +76,9 @@ SIGNATURES = {
     "ep_dispatch_with_layout": (ctypes.c_int, [c_void_p, c_void_p, c_void_p, c_void_p, ctypes.POINTER(EpLayout),
                                                ctypes.c_int, c_void_p, c_void_p, c_void_p,
                                                ctypes.POINTER(EpHandle), c_void_p]),
+    "ep_dispatch_with_layout_noalloc": (ctypes.c_int, [ctypes.POINTER(EpConfig), c_void_p, c_void_p, c_void_p,
+                                                       ctypes.POINTER(EpLayout), ctypes.c_int, c_void_p, c_void_p,
+                                                       c_void_p, ctypes.POINTER(EpHandle), c_void_p, c_void_p]),
     "ep_dispatch_dedup": (ctypes.c_int, [c_void_p, c_void_p, c_void_p, c_void_p, ctypes.POINTER(EpLayout),
                                          ctypes.c_int, c_void_p, c_void_p, c_void_p, c_void_p,
                                          ctypes.POINTER(EpHandle), c_void_p]),
@@ -179,6 +183,16 @@ def ep_dispatch_with_layout(ctx: int, x: int, topk_idx: int, topk_weights: Optio
     _check(load().ep_dispatch_with_layout(ctx, x, topk_idx, topk_weights, ctypes.byref(layout), int(use_fp8),
                                           recv_x, recv_scales, recv_w, ctypes.byref(handle), stream),
            "ep_dispatch_with_layout")
+
+
+def ep_dispatch_with_layout_noalloc(cfg: EpConfig, x: int, topk_idx: int, topk_weights: Optional[int],
+                                    layout: EpLayout, use_fp8: int, recv_x: int, recv_scales: Optional[int],
+                                    recv_w: Optional[int], handle: EpHandle, status: Optional[int],
+                                    stream: int) -> None:
+    _check(load().ep_dispatch_with_layout_noalloc(ctypes.byref(cfg), x, topk_idx, topk_weights,
+                                                  ctypes.byref(layout), int(use_fp8), recv_x, recv_scales, recv_w,
+                                                  ctypes.byref(handle), status, stream),
+           "ep_dispatch_with_layout_noalloc")
 
 
 def ep_dispatch_dedup(ctx: int, x: int, topk_idx: int, topk_weights: Optional[int], layout: EpLayout,

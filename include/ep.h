@@ -60,6 +60,7 @@ extern "C" {
 #define EP_ERR_ALIGN (-2) /* a row array is not 16-byte aligned */
 #define EP_ERR_HIP (-3)   /* a HIP runtime call failed */
 #define EP_ERR_NOMEM (-4) /* the workspace could not be allocated */
+#define EP_ERR_SCRATCH (-5) /* ep_dispatch_with_layout_noalloc: the workload needs more than its static workspace */
 
 /* sticky device status bits */
 #define EP_ST_BAD_EXPERT 1u /* an index outside [-1, E): that slot was dropped */
@@ -196,6 +197,27 @@ int ep_dispatch_with_layout(ep_ctx *ctx, const uint16_t *x, const int32_t *topk_
                             const float *topk_weights, const ep_layout *layout, int use_fp8,
                             void *recv_x, float *recv_scales, float *recv_w, ep_handle *handle,
                             ep_stream_t stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * call as ep_dispatch_with_layout, with the same outputs bit for bit, but
+ * without a context. *cfg describes the call (as for ep_create); the
+ * workspace is a static device array of 4 MiB that the library holds on
+ * each GPU it runs on until the process ends. The call allocates nothing
+ * (no hipMalloc, no hipFree). A cfg with more than 4096 layout tiles of 256
+ * tokens, or whose look-back states (tiles x (E + R) x 8 bytes) exceed the
+ * 3.4 MiB the array keeps for them, returns EP_ERR_SCRATCH without
+ * launching: up to about 400K tokens at 256 experts on 32 ranks, 105K at
+ * 1024 experts on 64 ranks. status: a device uint32 the kernels OR their EP_ST_* bits into
+ * (the caller clears it; NULL: not reported). Every call on one GPU shares
+ * that GPU's array and picks up where the last call left it (the array
+ * needs no clearing); calls that overlap on one GPU (two streams, two
+ * threads) race and give undefined results. Same argument, alignment and
+ * error rules as ep_dispatch_with_layout otherwise. */
+int ep_dispatch_with_layout_noalloc(const ep_config *cfg, const uint16_t *x, const int32_t *topk_idx,
+                                    const float *topk_weights, const ep_layout *layout, int use_fp8,
+                                    void *recv_x, float *recv_scales, float *recv_w, ep_handle *handle,
+                                    uint32_t *status, ep_stream_t stream);
 
 /* Rank-deduplicated dispatch (the pages' normal kernels send a token once
  * per destination rank): for every leader slot (t, j) of rank d (see

@@ -147,5 +147,12 @@ def test_new_entry_points_reject_null_without_gpu(lib):
                                            None) == ep.EP_ERR_ARG
     assert L.ep_set_cu_budget(None, 8) == ep.EP_ERR_ARG
     assert L.ep_set_spin_limit(None, 1) == ep.EP_ERR_ARG
+    # the no-allocation call refuses a workload beyond its static workspace
+    # before touching the GPU
+    big = ep.EpConfig(1 << 22, 8, 256, 32, 7168, 0, 1 << 20)
+    assert L.ep_dispatch_with_layout_noalloc(big, None, None, None, None, 1, None, None, None, None, None,
+                                             None) == ep.EP_ERR_SCRATCH
+    assert L.ep_dispatch_with_layout_noalloc(None, None, None, None, None, 1, None, None, None, None, None,
+                                             None) == ep.EP_ERR_ARG
     assert L.ep_cu_census(0, 0, None, None) == ep.EP_OK  # nothing to launch
     assert L.ep_cu_census(16, 65, None, None) == ep.EP_ERR_ARG
