@@ -72,6 +72,8 @@ def _bind(lib):
     lib.oracle_positions_dedup.argtypes = [i, i, i, i, ll, P, P, P, P]
     lib.oracle_ll_positions.restype = ctypes.c_uint32
     lib.oracle_ll_positions.argtypes = [i, i, i, i, P, P, P, P]
+    lib.oracle_prereduce.restype = None
+    lib.oracle_prereduce.argtypes = [i, ll, i, i, ll, ll, P, P, P, P, P, P]
     lib.oracle_dispatch_dedup.restype = None
     lib.oracle_dispatch_dedup.argtypes = [i, i, i, i, i, i, P, P, P, P, P, i, P, P, P, P]
     for name in ("oracle_e4m3_encode", "oracle_e4m3_decode", "oracle_bf16_round"):
@@ -296,6 +298,33 @@ class Oracle:
                                        _ptr(_c(pos, np.int32)), _ptr(tk), 0 if tk is None else tk.size,
                                        _ptr(recv_x), _ptr(recv_scales), _ptr(rti), _ptr(rtw))
         return recv_x, recv_scales, rti, rtw
+
+    # sentinel left in the rows the pre-reduction does not use (a NaN pattern
+    # that no bf16 rounding produces: quiet NaNs come out as 0x7fc0 | payload)
+    UNUSED_ROW = 0x7FBF
+
+    def prereduce(self, expert_out: np.ndarray, recv_topk_idx: np.ndarray, recv_topk_w: Optional[np.ndarray],
+                  token_rows: np.ndarray, R: int, cap_rows: int, row_lo: int = 0, row_hi: Optional[int] = None,
+                  return_acc: bool = False):
+        """Expert-side pre-reduction of deduplicated rows [row_lo, row_hi)
+        (default: all R*cap_rows). expert_out: [rows, k, H] bf16 bits for
+        those rows; recv_topk_idx / recv_topk_w: [rows, k]. Returns reduced
+        [rows, H] (UNUSED_ROW in rows that are not used) and, if asked, the
+        fp32 sums (NaN in unused rows)."""
+        row_hi = R * cap_rows if row_hi is None else row_hi
+        n = row_hi - row_lo
+        expert_out = _c(expert_out, np.uint16)
+        k, H = expert_out.shape[1], expert_out.shape[2]
+        assert expert_out.shape[0] == n
+        rti = _c(recv_topk_idx, np.int32)
+        assert rti.shape == (n, k)
+        rtw = None if recv_topk_w is None else _c(recv_topk_w, np.float32)
+        tr = _c(token_rows, np.int32)
+        reduced = np.full((n, H), self.UNUSED_ROW, np.uint16)
+        acc = np.full((n, H), np.nan, np.float32) if return_acc else None
+        self.lib.oracle_prereduce(R, int(cap_rows), k, H, int(row_lo), int(row_hi), _ptr(expert_out), _ptr(rti),
+                                  _ptr(rtw), _ptr(tr), _ptr(reduced), _ptr(acc))
+        return (reduced, acc) if return_acc else reduced
 
     def forward(self, x, topk_idx, topk_w, E: int, R: int, cap_rows: int, use_fp8: bool):
         """Layout + positions + dispatch, as one convenience call for tests."""

@@ -513,6 +513,50 @@ void oracle_combine(int T, int k, int H, const uint16_t *rows, const int32_t *po
     free(a);
 }
 
+/* Expert-side pre-reduction of the rank-deduplicated rows. Reading (the
+ * pages' normal kernels send a token once per destination rank, and the
+ * guide's combine brings the experts' outputs back to the token's rank):
+ * rank d holds one received row per token it serves; each of its experts
+ * that the token chose produces an output for that row, and the rank sums
+ * those outputs with the row's routing weights, so that combine sends one
+ * row back per (token, rank). Layout of the expert outputs: for received row
+ * p and slot j, expert_out[p][j][:] (bf16) is the output of the row's slot-j
+ * expert; only slots whose routing entry recv_topk_idx[p][j] is >= 0 are
+ * read. For every used row p of rank d (p - d*cap_rows below both
+ * token_rows[d] and cap_rows), channel i:
+ *   sum = +0.0f; for j = 0 .. k-1 with recv_topk_idx[p][j] >= 0:
+ *       sum = fmaf(weight, expert_out[p][j][i], sum)
+ *                     (weight = recv_topk_w[p][j], or 1 if recv_topk_w is NULL)
+ *   reduced[p][i] = bf16(sum)   (round to nearest even)
+ * the arithmetic of oracle_combine (fp32, one fused multiply-add per slot in
+ * slot order, one rounding). Rows that are not used are left untouched.
+ * Only rows [row_lo, row_hi) are computed; every array holds exactly those
+ * rows (row p at index p - row_lo). sums (optional) receives the fp32 sums. */
+void oracle_prereduce(int R, long long cap_rows, int k, int H, long long row_lo, long long row_hi,
+                      const uint16_t *expert_out, const int32_t *recv_topk_idx,
+                      const float *recv_topk_w, const int32_t *token_rows,
+                      uint16_t *reduced, float *sums) {
+    float *s = (float *)malloc(sizeof(float) * (size_t)(H > 0 ? H : 1));
+    for (long long p = row_lo; p < row_hi; ++p) {
+        long long d = p / cap_rows;
+        long long local = p - d * cap_rows;
+        if (d >= R || local >= (long long)token_rows[d]) continue; /* not a used row */
+        long long r = p - row_lo;
+        for (int i = 0; i < H; ++i) s[i] = 0.0f;
+        for (int slot = 0; slot < k; ++slot) {
+            if (recv_topk_idx[r * k + slot] < 0) continue;
+            float weight = recv_topk_w ? recv_topk_w[r * k + slot] : 1.0f;
+            const uint16_t *out = expert_out + ((size_t)r * k + slot) * (size_t)H;
+            for (int i = 0; i < H; ++i) s[i] = fmaf(weight, bf16_to_float(out[i]), s[i]);
+        }
+        for (int i = 0; i < H; ++i) {
+            reduced[(size_t)r * H + i] = bf16_from_float(s[i]);
+            if (sums) sums[(size_t)r * H + i] = s[i];
+        }
+    }
+    free(s);
+}
+
 /* combine_backward: the gradient of combined_x is sent along the same routes
  * as dispatch (a bf16 dispatch of grad_y reusing the forward handle):
  *   grad_rows[pos[t][j]][:] = grad_y[t][:] for every kept slot.

@@ -59,6 +59,11 @@ void oracle_combine(int T, int k, int H, const uint16_t *rows, const int32_t *po
                     const float *w, const int32_t *tokens, int ntokens,
                     uint16_t *y, float *acc);
 
+void oracle_prereduce(int R, long long cap_rows, int k, int H, long long row_lo, long long row_hi,
+                      const uint16_t *expert_out, const int32_t *recv_topk_idx,
+                      const float *recv_topk_w, const int32_t *token_rows,
+                      uint16_t *reduced, float *sums);
+
 void oracle_combine_backward(int T, int k, int H, const uint16_t *grad_y,
                              const int32_t *pos, uint16_t *grad_rows);
 

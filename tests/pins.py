@@ -648,10 +648,116 @@ def pin_dedup_dispatch(orc):
                     assert rtw[p, jj] == (w[t, jj] if here else 0.0)
 
 
+# ---------------------------------------------------------------------------
+# expert-side pre-reduction of deduplicated rows
+# ---------------------------------------------------------------------------
+
+def f32_nearest(fr):
+    """The fp32 value nearest to the rational fr, ties to the even pattern
+    (exact: candidates around numpy's double-rounded value compared as
+    fractions). Exact zeros come out as +0."""
+    from fractions import Fraction
+    if fr == 0:
+        return np.float32(0.0)
+    c = np.float32(float(fr))
+    cands = [np.nextafter(c, np.float32(-np.inf)), c, np.nextafter(c, np.float32(np.inf))]
+    return min(cands, key=lambda v: (abs(Fraction(float(v)) - fr), int(np.float32(v).view(np.uint32)) & 1))
+
+
+def fma32(a, b, c):
+    """fp32 fused multiply-add, a * b + c rounded once, by exact arithmetic."""
+    from fractions import Fraction
+    return f32_nearest(Fraction(float(a)) * Fraction(float(b)) + Fraction(float(c)))
+
+
+def pin_prereduce_golden(orc):
+    g = golden("layout_by_hand.json")
+    dd, pr = g["dedup"], g["prereduce"]
+    case = [c for c in dd["cases"] if c["cap_rows"] == pr["cap_rows"]][0]
+    R, H, k, cap = g["R"], g["H"], g["k"], pr["cap_rows"]
+    n = R * cap
+    rti = np.full((n, k), -1, np.int32)
+    for p, e in case["recv_topk_idx"].items():
+        rti[int(p)] = e
+    rtw = np.where(rti >= 0, np.array(pr["slot_weights"], np.float32)[None, :], 0.0).astype(np.float32)
+    vals = np.array([[8.0 * (p + 1) + (j + 1) for j in range(k)] for p in range(n)], np.float32)
+    eo = np.repeat(bf16_bits_of(vals)[:, :, None], H, 2)
+    tr = np.array(pr["token_rows"], np.int32)
+    red = orc.prereduce(eo, rti, rtw, tr, R, cap)
+    for p, v in pr["reduced"].items():
+        assert np.all(f32_of_bf16(red[int(p)]) == v), (p, f32_of_bf16(red[int(p)])[0], v)
+    for p in pr["unused_rows"]:
+        assert np.all(red[p] == orc.UNUSED_ROW), ("unused row written", p)
+    y = f32_of_bf16(orc.combine(red, np.array(case["pos"], np.int32), None))
+    assert np.array_equal(y, np.repeat(np.array(pr["combined"], np.float32)[:, None], H, 1)), y[:, 0]
+    # a row range computes the same rows
+    sub = orc.prereduce(eo[8:], rti[8:], rtw[8:], tr, R, cap, row_lo=8)
+    assert np.array_equal(sub, red[8:])
+
+
+def pin_prereduce_bruteforce(orc):
+    """fp32 fused multiply-adds in slot order, by exact arithmetic, on random
+    tiny inputs (random slot entries, weights and outputs, rows past
+    token_rows and capacity-limited ranks)."""
+    rng = np.random.default_rng(71)
+    for R, cap, k, H in ((2, 5, 3, 8), (3, 4, 4, 4), (1, 6, 2, 8), (4, 3, 5, 2)):
+        n = R * cap
+        rti = rng.integers(-1, 3, size=(n, k)).astype(np.int32)
+        rtw = rng.standard_normal((n, k)).astype(np.float32)
+        eo = bf16_bits_of(rng.standard_normal((n, k, H)).astype(np.float32))
+        tr = rng.integers(0, cap + 2, size=R).astype(np.int32)  # some ranks past their capacity
+        for weights in (rtw, None):
+            red, acc = orc.prereduce(eo, rti, weights, tr, R, cap, return_acc=True)
+            for p in range(n):
+                d, local = divmod(p, cap)
+                if local >= tr[d]:
+                    assert np.all(red[p] == orc.UNUSED_ROW) and np.all(np.isnan(acc[p])), ("row", p)
+                    continue
+                for i in range(H):
+                    s = np.float32(0.0)
+                    for j in range(k):
+                        if rti[p, j] >= 0:
+                            wj = np.float32(1.0) if weights is None else weights[p, j]
+                            s = fma32(wj, f32_of_bf16(eo[p, j, i]), s)
+                    assert acc[p, i].view(np.uint32) == np.float32(s).view(np.uint32), (p, i, acc[p, i], s)
+                    assert red[p, i] == bf16_bits_of(np.array([s], np.float32))[0], (p, i)
+
+
+def pin_prereduce_order_fma(orc):
+    """Slot order and one fused multiply-add per slot are part of the
+    definition: (2^24, 1, -2^24) sums to 0 in slot order, (-2^24, 1, 2^24) to
+    1; (1+2^-23)(1+2^-7) - 1 keeps its 2^-30 term."""
+    k, H = 3, 4
+    vals = np.array([[2.0 ** 24, 1.0, -(2.0 ** 24)], [-(2.0 ** 24), 1.0, 2.0 ** 24],
+                     [-1.0, 1.0 + 2.0 ** -7, 0.0]], np.float32)
+    eo = np.repeat(bf16_bits_of(vals)[:, :, None], H, 2)
+    rti = np.array([[0, 1, 2], [0, 1, 2], [0, 1, -1]], np.int32)
+    rtw = np.array([[1, 1, 1], [1, 1, 1], [1.0, 1.0 + 2.0 ** -23, 0]], np.float32)
+    red, acc = orc.prereduce(eo, rti, rtw, np.array([3], np.int32), 1, 3, return_acc=True)
+    assert np.all(acc[0] == 0.0) and np.all(acc[1] == 1.0), acc[:, 0]
+    assert np.all(acc[2] == np.float32(2.0 ** -7 + 2.0 ** -23 + 2.0 ** -30)), acc[2, 0]
+
+
+def pin_prereduce_fp64(orc):
+    """fp64 bound on a larger random case: |sum - sum_j w v| <= k 2^-24 sum_j |w v|."""
+    rng = np.random.default_rng(72)
+    R, cap, k, H = 4, 40, 8, 256
+    n = R * cap
+    rti = np.where(rng.random((n, k)) < 0.3, 1, -1).astype(np.int32)
+    rtw = rng.random((n, k)).astype(np.float32)
+    eo = bf16_bits_of(rng.standard_normal((n, k, H)).astype(np.float32))
+    tr = np.full(R, cap, np.int32)
+    _, acc = orc.prereduce(eo, rti, rtw, tr, R, cap, return_acc=True)
+    wv = np.where(rti[:, :, None] >= 0, rtw[:, :, None].astype(np.float64) * f32_of_bf16(eo).astype(np.float64), 0)
+    exact, mag = wv.sum(1), np.abs(wv).sum(1)
+    assert np.all(np.abs(acc.astype(np.float64) - exact) <= k * 2.0 ** -24 * mag + 1e-300)
+
+
 def pin_dedup_prereduce(orc):
     """Per-expert exchange vs deduplicated exchange with the expert side
-    pre-reducing (weighting and summing the outputs of a row's local experts):
-    on values exact in bf16 and fp32 both give the same combined result."""
+    pre-reducing (oracle_prereduce: weighting and summing the outputs of a
+    row's local experts): on values exact in bf16 and fp32 both give the same
+    combined result."""
     rng = np.random.default_rng(59)
     T, k, E, R, H = 48, 4, 16, 4, 128
     topk = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32)
@@ -666,7 +772,9 @@ def pin_dedup_prereduce(orc):
     rir, rows, _ = orc.layout_dedup(topk, E, R, cap)
     pdd, _ = orc.positions_dedup(topk, rir, E, R, cap)
     _, _, rti, rtw = orc.dispatch_dedup(np.zeros((T, H), np.uint16), topk, w, pdd, E, R, R * cap, False)
-    pre = np.zeros((R * cap, H), np.float32)
+    # each deduplicated row's slot outputs: the per-expert output of that
+    # (token, expert), i.e. what the rank's expert computes for the row
+    eo = np.zeros((R * cap, k, H), np.uint16)
     epr = E // R
     for t in range(T):
         for j in range(k):
@@ -674,10 +782,11 @@ def pin_dedup_prereduce(orc):
             if p < 0:
                 continue
             for jj in range(k):
-                if rti[p, jj] >= 0:  # expert rti + d*epr's output row for token t, weighted
+                if rti[p, jj] >= 0:
                     assert pos[t, jj] >= 0 and topk[t, jj] == rti[p, jj] + (p // cap) * epr
-                    pre[p] += rtw[p, jj] * f32_of_bf16(out[pos[t, jj]])
-    y_dd = orc.combine(bf16_bits_of(pre), pdd, None)
+                    eo[p, jj] = out[pos[t, jj]]
+    pre = orc.prereduce(eo, rti, rtw, rows, R, cap)
+    y_dd = orc.combine(pre, pdd, None)
     assert np.array_equal(y_dd, y_ref), "dedup + pre-reduction differs from the per-expert combine"
 
 
@@ -783,5 +892,6 @@ ALL_PINS = [
     pin_dispatch_bf16, pin_fp8_golden, pin_fp8_bound, pin_fp8_torch,
     pin_combine_fp64, pin_combine_order, pin_combine_fma, pin_combine_identity, pin_backward,
     pin_dedup_golden, pin_dedup_bruteforce, pin_dedup_dispatch, pin_dedup_prereduce,
+    pin_prereduce_golden, pin_prereduce_bruteforce, pin_prereduce_order_fma, pin_prereduce_fp64,
     pin_ll_golden, pin_ll_bruteforce, pin_ll_invariants,
 ]

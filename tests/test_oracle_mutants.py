@@ -91,6 +91,22 @@ MUTANTS = [
      "recv_topk_w[(size_t)p * k + jj] = topk_w[(size_t)t * k + jj];"),
     ("dedup positions keep the row at cap", "if (r < 0 || (long long)r >= cap_rows) {",
      "if (r < 0 || (long long)r > cap_rows) {"),
+    # expert-side pre-reduction
+    ("prereduce drops the last slot", "        for (int slot = 0; slot < k; ++slot) {",
+     "        for (int slot = 0; slot < k - 1; ++slot) {"),
+    ("prereduce reversed slot order", "        for (int slot = 0; slot < k; ++slot) {",
+     "        for (int slot = k - 1; slot >= 0; --slot) {"),
+    ("prereduce ignores the weights", "float weight = recv_topk_w ? recv_topk_w[r * k + slot] : 1.0f;",
+     "float weight = 1.0f;"),
+    ("prereduce reads the next slot's output",
+     "const uint16_t *out = expert_out + ((size_t)r * k + slot) * (size_t)H;",
+     "const uint16_t *out = expert_out + ((size_t)r * k + (slot + 1) % k) * (size_t)H;"),
+    ("prereduce unfused", "for (int i = 0; i < H; ++i) s[i] = fmaf(weight, bf16_to_float(out[i]), s[i]);",
+     "for (int i = 0; i < H; ++i) s[i] = s[i] + weight * bf16_to_float(out[i]);"),
+    ("prereduce writes unused rows", "if (d >= R || local >= (long long)token_rows[d]) continue; /* not a used row */",
+     "if (d >= R) continue;"),
+    ("prereduce rank from the range-relative row", "        long long d = p / cap_rows;",
+     "        long long d = (p - row_lo) / cap_rows;"),
     ("combine_backward copies the wrong token",
      "memcpy(grad_rows + (size_t)p * H, grad_y + (size_t)t * H, sizeof(uint16_t) * (size_t)H);",
      "memcpy(grad_rows + (size_t)p * H, grad_y + (size_t)((t + 1) % T) * H, sizeof(uint16_t) * (size_t)H);"),
