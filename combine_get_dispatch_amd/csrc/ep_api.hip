@@ -162,7 +162,46 @@ int combine_common(ep_ctx *ctx, const uint16_t *rows, const ep_handle *h, const 
     if (ctx->debug)
         std::fprintf(stderr, "libep: %s T=%d k=%d H=%d waves=%d (%d/token, %d passes each)\n", name, a.T, a.k,
                      a.H, g.num_waves, g.wpt, g.ppw);
-    return hip_fail(ep::launch_combine(a, out_f32, g.num_waves, (hipStream_t)stream), name);
+    return hip_fail(ep::launch_combine(a, out_f32, false, g.num_waves, (hipStream_t)stream), name);
+}
+
+// The expert-side pre-reduction of deduplicated rows: the combine kernel over
+// the received rows (see ep_prereduce in ep.h).
+int prereduce_common(ep_ctx *ctx, const uint16_t *expert_out, const int32_t *recv_topk_idx,
+                     const float *recv_topk_w, const int32_t *token_rows, void *out, bool out_f32,
+                     ep_stream_t stream, const char *name) {
+    if (!ctx) return EP_ERR_ARG;
+    if (int r = check_device(ctx)) return r;
+    const ep_config &c = ctx->cfg;
+    const int64_t rows = (int64_t)c.num_ranks * c.cap_rows;
+    if (rows == 0) return EP_OK;
+    if (rows * c.num_topk >= ((int64_t)1 << 31)) return EP_ERR_ARG;  // per-(row, slot) outputs indexed by int
+    if (!expert_out || !recv_topk_idx || !token_rows || !out) return EP_ERR_ARG;
+    if (!aligned(expert_out, 16) || !aligned(out, 16) || !aligned(recv_topk_idx, 4) || !aligned(recv_topk_w, 4) ||
+        !aligned(token_rows, 4))
+        return EP_ERR_ALIGN;
+    const Geometry g = geometry((int)rows, c.hidden, kCombineTargetWaves);
+    ep::CombineArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.rows = expert_out;
+    a.pos = recv_topk_idx;
+    a.w = recv_topk_w;
+    a.out = out;
+    a.T = (int)rows;
+    a.k = c.num_topk;
+    a.H = c.hidden;
+    a.num_rows = rows * c.num_topk;
+    a.token_rows = token_rows;
+    a.cap_rows = c.cap_rows;
+    a.waves_per_token = g.wpt;
+    a.passes_per_wave = g.ppw;
+    a.npass = g.npass;
+    a.counters = ctx->counters;
+    a.status = ctx->status;
+    if (ctx->debug)
+        std::fprintf(stderr, "libep: %s rows=%lld k=%d H=%d waves=%d\n", name, (long long)rows, a.k, a.H,
+                     g.num_waves);
+    return hip_fail(ep::launch_combine(a, out_f32, true, g.num_waves, (hipStream_t)stream), name);
 }
 
 // log2(v) when v is a power of two, else -1
@@ -680,6 +719,18 @@ int ep_combine(ep_ctx *ctx, const uint16_t *expert_out, const ep_handle *handle,
 int ep_combine_f32(ep_ctx *ctx, const uint16_t *expert_out, const ep_handle *handle, const float *weights,
                    float *combined_f32, ep_stream_t stream) {
     return combine_common(ctx, expert_out, handle, weights, combined_f32, true, stream, "ep_combine_f32");
+}
+
+int ep_prereduce(ep_ctx *ctx, const uint16_t *expert_out, const int32_t *recv_topk_idx, const float *recv_topk_w,
+                 const int32_t *token_rows, uint16_t *reduced, ep_stream_t stream) {
+    return prereduce_common(ctx, expert_out, recv_topk_idx, recv_topk_w, token_rows, reduced, false, stream,
+                            "ep_prereduce");
+}
+
+int ep_prereduce_f32(ep_ctx *ctx, const uint16_t *expert_out, const int32_t *recv_topk_idx,
+                     const float *recv_topk_w, const int32_t *token_rows, float *reduced_f32, ep_stream_t stream) {
+    return prereduce_common(ctx, expert_out, recv_topk_idx, recv_topk_w, token_rows, reduced_f32, true, stream,
+                            "ep_prereduce_f32");
 }
 
 int ep_combine_backward(ep_ctx *ctx, const uint16_t *grad_combined, const ep_handle *handle,

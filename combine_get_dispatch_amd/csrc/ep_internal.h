@@ -69,12 +69,14 @@ struct DispatchArgs {
 };
 
 struct CombineArgs {
-    const uint16_t *rows;  // [R*cap][H] bf16
-    const int32_t *pos;    // [T][k]
+    const uint16_t *rows;  // [R*cap][H] bf16 (pre-reduction: [R*cap][k][H], one row per (received row, slot))
+    const int32_t *pos;    // [T][k] (pre-reduction: the rows' routing entries [R*cap][k], slot read if >= 0)
     const float *w;        // [T][k] or NULL
     void *out;             // [T][H] bf16 or fp32
-    int T, k, H;
+    int T, k, H;           // (pre-reduction: T = R*cap received rows)
     int64_t num_rows;      // rows of `rows`; positions outside are skipped
+    const int32_t *token_rows;  // pre-reduction: [R] used rows per rank
+    int64_t cap_rows;           // pre-reduction: rows per rank
     int waves_per_token, passes_per_wave, npass;
     uint32_t *counters;
     uint32_t *status;      // sticky EP_ST_* bits
@@ -92,7 +94,9 @@ hipError_t launch_dispatch_inblock(const LayoutArgs &la, const DispatchArgs &da,
 hipError_t launch_layout_dispatch(const LayoutArgs &la, const DispatchArgs &da, bool fp8, int mode, int num_waves,
                                   int resident_blocks, hipStream_t s);
 int layout_dispatch_blocks_per_cu(int k, bool fp8, int mode, size_t lds);
-hipError_t launch_combine(const CombineArgs &a, bool out_f32, int num_waves, hipStream_t s);
+// prereduce: a.pos holds the received rows' routing entries and a.rows the
+// per-(row, slot) expert outputs (see CombineArgs)
+hipError_t launch_combine(const CombineArgs &a, bool out_f32, bool prereduce, int num_waves, hipStream_t s);
 hipError_t launch_copy(const void *src, void *dst, size_t n16, hipStream_t s);
 hipError_t launch_cu_census(int blocks, int naps, uint32_t *ids, hipStream_t s);
 // low-latency dispatch: a.T % R == 0, a.T / R <= kLayoutTile, rows e*T + s*(T/R) + r

@@ -1445,19 +1445,30 @@ __global__ __launch_bounds__(kTileTokens) void k_layout_dispatch(LayoutArgs la, 
 
 constexpr int kSlotChunk = 8;
 
-template <bool OUT_F32>
+// PREREDUCE: the expert-side pre-reduction of rank-deduplicated rows, the
+// same arithmetic over other indices. "Token" t is received row p of rank
+// d = p / cap_rows (the wave ends if p is past token_rows[d]); its slot j is
+// read when the row's routing entry pos[p][j] (the local expert) is >= 0,
+// from row p*k + j of the per-(row, slot) expert outputs.
+template <bool OUT_F32, bool PREREDUCE>
 __global__ __launch_bounds__(kWavesPerBlock * 64) void k_combine(CombineArgs a) {
     const int lane = threadIdx.x & 63;
     const int gw = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
     const int t = gw / a.waves_per_token;
     const int part = gw - t * a.waves_per_token;
     if (t >= a.T) return;
+    if (PREREDUCE) {
+        const int64_t d = t / a.cap_rows;
+        if (t - d * a.cap_rows >= (int64_t)a.token_rows[d]) return;  // not a used row (whole wave)
+    }
 
     int p = -1;
     float wt = 1.0f;
     if (lane < a.k) {
         p = a.pos[(size_t)t * a.k + lane];
-        if (p < -1 || p >= a.num_rows) {  // not a position this buffer holds
+        if (PREREDUCE) {
+            p = p >= 0 ? t * a.k + lane : -1;
+        } else if (p < -1 || p >= a.num_rows) {  // not a position this buffer holds
             atomicOr(a.status, kStBadHandle);
             p = -1;
         }
@@ -1689,12 +1700,11 @@ hipError_t launch_dispatch(const DispatchArgs &a, bool fp8, int mode, int num_wa
     return hipGetLastError();
 }
 
-hipError_t launch_combine(const CombineArgs &a, bool out_f32, int num_waves, hipStream_t s) {
+hipError_t launch_combine(const CombineArgs &a, bool out_f32, bool prereduce, int num_waves, hipStream_t s) {
     const dim3 grid((num_waves + kWavesPerBlock - 1) / kWavesPerBlock), block(kWavesPerBlock * 64);
-    if (out_f32)
-        hipLaunchKernelGGL(k_combine<true>, grid, block, 0, s, a);
-    else
-        hipLaunchKernelGGL(k_combine<false>, grid, block, 0, s, a);
+    static void (*const kernels[4])(CombineArgs) = {k_combine<false, false>, k_combine<true, false>,
+                                                     k_combine<false, true>, k_combine<true, true>};
+    hipLaunchKernelGGL(kernels[(out_f32 ? 1 : 0) + (prereduce ? 2 : 0)], grid, block, 0, s, a);
     return hipGetLastError();
 }
 

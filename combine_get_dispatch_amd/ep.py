@@ -92,6 +92,8 @@ SIGNATURES = {
                                   c_void_p]),
     "ep_combine_f32": (ctypes.c_int, [c_void_p, c_void_p, ctypes.POINTER(EpHandle), c_void_p,
                                       c_void_p, c_void_p]),
+    "ep_prereduce": (ctypes.c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "ep_prereduce_f32": (ctypes.c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
     "ep_combine_backward": (ctypes.c_int, [c_void_p, c_void_p, ctypes.POINTER(EpHandle), c_void_p,
                                            c_void_p]),
     "ep_dispatch_backward": (ctypes.c_int, [c_void_p, c_void_p, ctypes.POINTER(EpHandle), c_void_p,
@@ -284,6 +286,18 @@ def ep_set_cu_budget(ctx: int, num_cus: int) -> None:
 
 def ep_set_spin_limit(ctx: int, polls: int) -> None:
     _check(load().ep_set_spin_limit(ctx, polls), "ep_set_spin_limit")
+
+
+def ep_prereduce(ctx: int, expert_out: int, recv_topk_idx: int, recv_topk_w: Optional[int], token_rows: int,
+                 reduced: int, stream: int) -> None:
+    _check(load().ep_prereduce(ctx, expert_out, recv_topk_idx, recv_topk_w, token_rows, reduced, stream),
+           "ep_prereduce")
+
+
+def ep_prereduce_f32(ctx: int, expert_out: int, recv_topk_idx: int, recv_topk_w: Optional[int], token_rows: int,
+                     reduced: int, stream: int) -> None:
+    _check(load().ep_prereduce_f32(ctx, expert_out, recv_topk_idx, recv_topk_w, token_rows, reduced, stream),
+           "ep_prereduce_f32")
 
 
 def ep_stream_destroy(stream: int) -> None:
@@ -523,6 +537,23 @@ class Buffer:
     def combine_f32(self, expert_out, handle: Handle, weights=None, out=None):
         out = out if out is not None else self._empty((self.T, self.H), self.torch.float32)
         ep_combine_f32(self.ctx, expert_out.data_ptr(), handle.c(), _ptr(weights), out.data_ptr(), _stream())
+        return out
+
+    def prereduce(self, expert_out, recv_topk_idx, recv_topk_w, token_rows, out=None):
+        """Expert-side pre-reduction of deduplicated rows: expert_out
+        [R*cap_rows, k, H] bf16 (the output of each received row's slot-j
+        expert), routing entries and weights from dispatch_dedup, token_rows
+        from the deduplicated layout. Returns reduced [R*cap_rows, H] bf16
+        (unused rows not written)."""
+        out = out if out is not None else self._empty((self.num_rows, self.H), self.torch.bfloat16)
+        ep_prereduce(self.ctx, expert_out.data_ptr(), recv_topk_idx.data_ptr(), _ptr(recv_topk_w),
+                     token_rows.data_ptr(), out.data_ptr(), _stream())
+        return out
+
+    def prereduce_f32(self, expert_out, recv_topk_idx, recv_topk_w, token_rows, out=None):
+        out = out if out is not None else self._empty((self.num_rows, self.H), self.torch.float32)
+        ep_prereduce_f32(self.ctx, expert_out.data_ptr(), recv_topk_idx.data_ptr(), _ptr(recv_topk_w),
+                         token_rows.data_ptr(), out.data_ptr(), _stream())
         return out
 
     def combine_backward(self, grad_combined, handle: Handle, out=None):

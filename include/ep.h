@@ -285,6 +285,30 @@ int ep_combine(ep_ctx *ctx, const uint16_t *expert_out, const ep_handle *handle,
 int ep_combine_f32(ep_ctx *ctx, const uint16_t *expert_out, const ep_handle *handle,
                    const float *weights, float *combined_f32, ep_stream_t stream);
 
+/* Expert-side pre-reduction of rank-deduplicated rows (the pages' normal
+ * kernels send a token once per destination rank; the guide's combine brings
+ * the experts' outputs back to the token's rank, [Guide] section 5). Rank d
+ * sums, for each row it received, the outputs of its experts that the token
+ * chose, weighted by the row's routing weights, so that ep_combine (weights
+ * NULL, on the deduplicated handle) sends one row back per (token, rank).
+ * expert_out: [R*cap_rows][k][H] bf16, entry (p, j) the output of received
+ * row p's slot-j expert; only slots with recv_topk_idx[p][j] >= 0 are read
+ * (the others may hold anything). recv_topk_idx / recv_topk_w: [R*cap_rows][k]
+ * from ep_dispatch_dedup (recv_topk_w NULL: weights 1). token_rows: [R] from
+ * the deduplicated layout; row p of rank d = p / cap_rows is used when
+ * p - d*cap_rows < token_rows[d]. For each used row and channel i:
+ *   sum = +0.0f; for j = 0 .. k-1 with recv_topk_idx[p][j] >= 0:
+ *       sum = fmaf(recv_topk_w[p][j], expert_out[p][j][i], sum)
+ *   reduced[p][i] = bf16_rne(sum)
+ * (ep_combine's arithmetic). Unused rows of reduced are not written.
+ * reduced: [R*cap_rows][H] bf16. Requires R*cap_rows*k < 2^31; rows arrays
+ * 16-byte aligned. Returns EP_OK, EP_ERR_ARG, EP_ERR_ALIGN or EP_ERR_HIP.
+ * ep_prereduce_f32 writes the fp32 sums instead (for checking). */
+int ep_prereduce(ep_ctx *ctx, const uint16_t *expert_out, const int32_t *recv_topk_idx,
+                 const float *recv_topk_w, const int32_t *token_rows, uint16_t *reduced, ep_stream_t stream);
+int ep_prereduce_f32(ep_ctx *ctx, const uint16_t *expert_out, const int32_t *recv_topk_idx,
+                     const float *recv_topk_w, const int32_t *token_rows, float *reduced_f32, ep_stream_t stream);
+
 /* combine_backward (the guide: backward reuses the forward handle): the
  * gradient of combined_x travels the dispatch routes, i.e. a bf16 dispatch
  * of grad_combined [T][H] into grad_rows [R*cap_rows][H] reusing handle->pos

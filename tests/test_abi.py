@@ -147,6 +147,8 @@ def test_new_entry_points_reject_null_without_gpu(lib):
                                            None) == ep.EP_ERR_ARG
     assert L.ep_set_cu_budget(None, 8) == ep.EP_ERR_ARG
     assert L.ep_set_spin_limit(None, 1) == ep.EP_ERR_ARG
+    assert L.ep_prereduce(None, None, None, None, None, None, None) == ep.EP_ERR_ARG
+    assert L.ep_prereduce_f32(None, None, None, None, None, None, None) == ep.EP_ERR_ARG
     # the no-allocation call refuses a workload beyond its static workspace
     # before touching the GPU
     big = ep.EpConfig(1 << 22, 8, 256, 32, 7168, 0, 1 << 20)
