@@ -58,6 +58,9 @@ def parse():
     p.add_argument("--dedup", action="store_true",
                    help="time the rank-deduplicated form as the step (layout, one row per (token, rank), "
                         "combine of the pre-reduced rows); implies --no-extras")
+    p.add_argument("--record-counters", nargs="+", metavar="PASS_DIR",
+                   help="summarize rocprofv3 --pmc runs of this bench (one counter set per run, "
+                        "--output-format csv; the sets of COUNTER_PASSES) into profiles/")
     p.add_argument("--record-traffic", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "TRACE_DIR"),
                    help="summarize rocprofv3 runs of this bench (--pmc FETCH_SIZE, --pmc WRITE_SIZE, "
                         "--kernel-trace --stats, all with --output-format csv) into profiles/")
@@ -157,22 +160,27 @@ class LlPath:
         self.buf.combine(self.expert_out, self.handle, self.main.w, out=self.y)
 
 
-def dedup_bytes(T, k, H, Nd, use_fp8):
+def dedup_bytes(T, k, H, Nd, N, use_fp8):
     """Algorithmic bytes of the rank-deduplicated step (Nd = rows, one per
-    (token, destination rank)): dispatch reads x and the weights, writes the
-    rows (+ scales) and each row's k routing entries (index + weight); the
-    combine of the pre-reduced rows reads them and writes y."""
+    (token, destination rank); N = kept (token, expert) slots): dispatch
+    reads x and the weights, writes the rows (+ scales) and each row's k
+    routing entries (index + weight); the expert-side pre-reduction reads the
+    N expert outputs of the rows' kept slots and the rows' routing entries
+    and writes the Nd reduced rows; the combine of the reduced rows reads them
+    and writes y. Returns (dispatch, pre-reduction, combine)."""
     G = H // 128
     row = H + 4 * G if use_fp8 else 2 * H
     d = 2 * T * H + Nd * row + 8 * Nd * k + 4 * T * k
+    pre = 2 * N * H + 8 * Nd * k + 2 * Nd * H
     c = 2 * Nd * H + 2 * T * H + 4 * T * k
-    return d, c
+    return d, pre, c
 
 
 class DedupPath:
     """The rank-deduplicated form of a workload's step: layout with the
-    leader ranks, one row per (token, destination rank), combine of the
-    pre-reduced rows (unit weights)."""
+    leader ranks, one row per (token, destination rank), the expert-side
+    pre-reduction of each row's expert outputs (per (row, slot), N(0,1)
+    bf16), and the combine of the reduced rows (unit weights)."""
 
     def __init__(self, main, torch, ep, workloads, seed):
         cfg = main.cfg
@@ -191,7 +199,8 @@ class DedupPath:
         self.recv_topk_idx = torch.empty((n, cfg.k), dtype=torch.int32, device="cuda")
         self.recv_topk_w = torch.empty((n, cfg.k), dtype=torch.float32, device="cuda")
         self.handle = b.new_handle()
-        self.expert_out = workloads.device_normal_bf16((n, cfg.H), seed=seed + 303)
+        self.expert_out = workloads.device_normal_bf16((n, cfg.k, cfg.H), seed=seed + 303)
+        self.reduced = torch.empty((n, cfg.H), dtype=torch.bfloat16, device="cuda")
         self.y = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device="cuda")
 
     def layout_op(self):
@@ -209,8 +218,12 @@ class DedupPath:
                                             out=(self.recv_x, self.recv_scales, self.recv_topk_idx,
                                                  self.recv_topk_w, self.handle))
 
+    def prereduce_op(self):
+        self.buf.prereduce(self.expert_out, self.recv_topk_idx, self.recv_topk_w, self.layout.token_rows,
+                           out=self.reduced)
+
     def combine_op(self):
-        self.buf.combine(self.expert_out, self.handle, None, out=self.y)
+        self.buf.combine(self.reduced, self.handle, None, out=self.y)
 
     def rows(self):
         return int((self.handle.pos >= 0).sum().item())
@@ -513,7 +526,7 @@ KERNELS = {  # regular expressions on the kernel names rocprofv3 reports
     "k_layout": r"k_layout<", "k_layout_dispatch": r"k_layout_dispatch<\d+, \w+, 1>",
     "k_layout_dispatch_dedup": r"k_layout_dispatch<\d+, \w+, 2>", "k_dispatch": r"k_dispatch<true, 1(, \w+)?>",
     "k_dispatch_dedup": r"k_dispatch<true, 2(, \w+)?>", "k_ll_dispatch": r"k_ll_dispatch<",
-    "k_combine": r"k_combine<false>", "k_copy": r"k_copy"}
+    "k_combine": r"k_combine<false, false>", "k_prereduce": r"k_combine<false, true>", "k_copy": r"k_copy"}
 
 
 def _csv_rows(d, suffix):
@@ -536,6 +549,79 @@ def _per_kernel(rows, value_key):
             if re.search(pat, r["Kernel_Name"]):
                 out[k].append((int(r["Grid_Size"]), float(r[value_key])))
     return out
+
+
+# One rocprofv3 --pmc run per set (a run holds at most 4 TCC and 8 SQ counters).
+COUNTER_PASSES = [
+    "MeanOccupancyPerCU MeanOccupancyPerActiveCU OccupancyPercent",
+    "TCC_EA0_RDREQ_sum TCC_EA0_RDREQ_LEVEL_sum TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum TCC_TAG_STALL_sum",
+    "TCC_EA0_WRREQ_sum TCC_EA0_WRREQ_LEVEL_sum TCC_EA0_WRREQ_DRAM_CREDIT_STALL_sum TCC_EA0_WRREQ_STALL_sum",
+    "TCC_EA0_WRREQ_64B_sum TCC_TOO_MANY_EA_WRREQS_STALL_sum TCC_EA0_RDREQ_128B_sum TCC_EA0_RDREQ_64B_sum",
+]
+# waves per SIMD the code objects allow (VGPRs), for the occupancy bound
+# (compiler resource-usage remarks of this build: k_layout<8> and the top-8 fused
+# grids 113 VGPRs, the FP8 per-expert dispatch 91, the per-rank one 99, the
+# combine 92, the one-pass top-8 FP8 low-latency dispatch 56, the copy 10)
+WAVES_PER_SIMD_BOUND = {"k_layout": 4, "k_layout_dispatch": 4, "k_layout_dispatch_dedup": 4, "k_dispatch": 5,
+                        "k_dispatch_dedup": 4, "k_ll_dispatch": 8, "k_combine": 5, "k_prereduce": 5, "k_copy": 8}
+
+
+def record_counters(args, cfg):
+    """Per-kernel means of the counters in the given rocprofv3 --pmc output
+    directories, and what they imply: occupancy against the code objects'
+    bound, mean L2-to-memory read and write latency, DRAM credit stall
+    cycles per request, request sizes. Writes profiles/<workload>_counters.md."""
+    vals = {}
+    passes = []
+    for d in args.record_counters:
+        rows = _csv_rows(d, "counter_collection.csv")
+        names = sorted({r["Counter_Name"] for r in rows})
+        passes.append(" ".join(names))
+        for k, pat in KERNELS.items():
+            for r in rows:
+                if re.search(pat, r["Kernel_Name"]):
+                    vals.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    mean = lambda xs: sum(xs) / len(xs)
+    cmd = (f"python3 bench.py --config {cfg.name}{mode_flags(args)} --steps {args.steps} --warmup {args.warmup} "
+           "--no-cpu-baseline --no-decode --no-extras")
+    lines = [f"# {cfg.name}{mode_flags(args).replace(' --', '_')}: occupancy and memory-request counters (rocprofv3)",
+             "", f"Workload: {cfg.desc}.", "",
+             "Commands (run from /tmp with TMPDIR=/tmp; the bench runs from the repository root), one run per "
+             "counter set:", ""]
+    for i, ps in enumerate(passes):
+        lines.append(f"    rocprofv3 --pmc {ps} --output-format csv -d <pass{i + 1}> -o run -- {cmd}")
+    lines += [f"    python3 bench.py --config {cfg.name}{mode_flags(args)} --steps {args.steps} --warmup {args.warmup} "
+              "--record-counters " + " ".join(f"<pass{i + 1}>" for i in range(len(passes))), "",
+              "Means over the profiled launches of each kernel. Occupancy: OccupancyPercent is the mean of "
+              "resident waves over a CU's 32 wave slots (4 SIMDs x 8) while the kernel runs; the bound is what "
+              "the code object's VGPR count allows. Latencies are TCC (L2) cycles from a request leaving L2 to "
+              "its return (LEVEL / REQ); credit stalls are cycles summed over the L2 channels.", "",
+              "| kernel | launches | occupancy % | waves/CU | VGPR bound waves/CU | read latency | write latency | "
+              "read credit stall / req | write credit stall / req | 128B reads % | 64B writes % |",
+              "|---|---|---|---|---|---|---|---|---|---|---|"]
+    for k, c in vals.items():
+        g = lambda n: mean(c[n]) if n in c else None
+        occ = g("OccupancyPercent")
+        rd, rdl, rds = g("TCC_EA0_RDREQ_sum"), g("TCC_EA0_RDREQ_LEVEL_sum"), g("TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum")
+        wr, wrl, wrs = g("TCC_EA0_WRREQ_sum"), g("TCC_EA0_WRREQ_LEVEL_sum"), g("TCC_EA0_WRREQ_DRAM_CREDIT_STALL_sum")
+        r128, w64 = g("TCC_EA0_RDREQ_128B_sum"), g("TCC_EA0_WRREQ_64B_sum")
+        f = lambda v, fmt: "-" if v is None else fmt.format(v)
+        div = lambda a, b: None if a is None or not b else a / b
+        nl = max(len(v) for v in c.values())
+        bound = WAVES_PER_SIMD_BOUND.get(k)
+        lines.append(f"| `{k}` | {nl} | {f(occ, '{:.1f}')} | {f(None if occ is None else occ * 32 / 100, '{:.1f}')} | "
+                     f"{f(None if bound is None else 4 * bound, '{:d}')} | {f(div(rdl, rd), '{:.0f}')} | "
+                     f"{f(div(wrl, wr), '{:.0f}')} | {f(div(rds, rd), '{:.3f}')} | {f(div(wrs, wr), '{:.3f}')} | "
+                     f"{f(None if div(r128, rd) is None else 100 * div(r128, rd), '{:.1f}')} | "
+                     f"{f(None if div(w64, wr) is None else 100 * div(w64, wr), '{:.1f}')} |")
+    lines += ["", "Raw means per kernel:", ""]
+    for k, c in vals.items():
+        lines.append(f"- `{k}`: " + ", ".join(f"{n} {mean(v):.4g}" for n, v in sorted(c.items())))
+    lines += ["", f"Kernel sources: sha256 prefix {source_sha()} (ep_kernels.hip, ep_api.hip, ep_internal.h)."]
+    path = os.path.join(PROFILES, f"{traffic_key(cfg, args)}_counters.md")
+    with open(path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    return path
 
 
 def traffic_key(cfg, args):
@@ -713,6 +799,10 @@ def main():
         from dataclasses import replace
         cfg = replace(cfg, T=cfg.T * cfg.R)
     K, W = args.steps, args.warmup
+    if args.record_counters:
+        # no GPU work: summarize the profiler output of earlier runs of this bench
+        print(record_counters(args, cfg))
+        return
     if args.record_traffic:
         # no GPU work: summarize the profiler output of an earlier run of this bench
         import numpy as np
@@ -724,13 +814,13 @@ def main():
         tk = wl.topk_idx
         t_of = np.repeat(np.arange(cfg.T), cfg.k).reshape(tk.shape)
         Nd = int(np.unique((t_of * cfg.R + tk // epr)[tk >= 0]).size)
-        dd_b, dc_b = dedup_bytes(cfg.T, cfg.k, cfg.H, Nd, cfg.use_fp8)
+        dd_b, dp_b, dc_b = dedup_bytes(cfg.T, cfg.k, cfg.H, Nd, N, cfg.use_fp8)
         if args.dedup:  # the step's combine reads the deduplicated rows
             c_b = dc_b
         res, trace = record_traffic(args, cfg, (c_b // 2) // 16 * 16)  # the copy the bench ran
         write_profile_summaries(args, cfg, res, trace, {"k_layout_dispatch": d_b, "k_dispatch": d_b, "k_combine": c_b,
                                                         "k_ll_dispatch": d_b, "k_dispatch_dedup": dd_b,
-                                                        "k_layout_dispatch_dedup": dd_b})
+                                                        "k_layout_dispatch_dedup": dd_b, "k_prereduce": dp_b})
         print(json.dumps(res))
         return
 
@@ -748,10 +838,16 @@ def main():
             return [f.dispatch_op, f.combine_op], f.buf, f
         if args.dedup:
             f = DedupPath(path, torch, ep, workloads, args.seed)
-            return ([f.layout_op, f.dispatch_op, f.combine_op] if args.separate else [f.fused_op, f.combine_op]), \
-                f.buf, f
+            return ([f.layout_op, f.dispatch_op, f.prereduce_op, f.combine_op] if args.separate else
+                    [f.fused_op, f.prereduce_op, f.combine_op]), f.buf, f
         return ([path.fused_op, path.combine_op] if fused else
                 [path.layout_op, path.dispatch_op, path.combine_op]), path.buf, path
+
+    # the ops of the step, by name, in order
+    op_names = (["ll_dispatch", "combine"] if args.ll else
+                (["layout", "dispatch"] if args.separate else ["layout_dispatch"]) + ["prereduce", "combine"]
+                if args.dedup else
+                ["layout_dispatch", "combine"] if fused else ["layout", "dispatch", "combine"])
 
     # Rotated buffers: consecutive steps use independent sets of inputs and
     # buffers, enough sets that together they exceed the 256 MB memory-side
@@ -768,10 +864,8 @@ def main():
     # pooled over the sets; the step itself with --eager)
     op_stats = []
     eager_ms, per_op = timed_rotating(torch, [st[0] for st in steps], K, W, op_stats)
-    if len(per_op) == 2:
-        ld_ms, com_ms = per_op
-    else:
-        lay_ms, dis_ms, com_ms = per_op
+    op_ms = dict(zip(op_names, per_op))
+    com_ms = op_ms["combine"]
     if args.eager:
         ms, ms_events, per_graph = eager_ms, eager_ms, 0
     else:
@@ -788,9 +882,11 @@ def main():
     else:
         N = main_path.kept_slots()
     d_bytes, c_bytes, cb_bytes = algo_bytes(cfg.T, cfg.k, cfg.H, N, cfg.use_fp8)
-    if dedp is not None:
-        d_bytes, c_bytes = dedup_bytes(cfg.T, cfg.k, cfg.H, N, cfg.use_fp8)
-    value = (d_bytes + c_bytes) / (ms * 1e-3) / 1e9
+    p_bytes = 0
+    if dedp is not None:  # N: deduplicated rows; the pre-reduction reads the kept slots' outputs
+        d_bytes, p_bytes, c_bytes = dedup_bytes(cfg.T, cfg.k, cfg.H, N, int((main_path.topk >= 0).sum().item()),
+                                                cfg.use_fp8)
+    value = (d_bytes + p_bytes + c_bytes) / (ms * 1e-3) / 1e9
     # the dominant kernel's duration: K of its launches, cycling through the
     # rotated sets, back to back between two HIP events on its stream (no
     # event between launches, whose queue latency would be counted, and no
@@ -820,9 +916,10 @@ def main():
                    "ranks_simulated": cfg.R, "topk": cfg.k, "routing": cfg.routing,
                    "fp8_dispatch": cfg.use_fp8, "cap_rows": step_buf.cap_rows, "kept_slots": N,
                    "step": ("low-latency dispatch launch, then combine" if llp is not None else
-                            "rank-deduplicated layout, dispatch, combine (three launches)"
+                            "rank-deduplicated layout, dispatch, expert-side pre-reduction, combine (four launches)"
                             if dedp is not None and args.separate else
-                            "fused rank-deduplicated layout+dispatch launch, then combine" if dedp is not None else
+                            "fused rank-deduplicated layout+dispatch launch, expert-side pre-reduction, combine"
+                            if dedp is not None else
                             "fused layout+dispatch launch, then combine" if fused
                             else "layout, dispatch, combine (three launches)") +
                            ("; eager launches" if args.eager else
@@ -842,23 +939,25 @@ def main():
         "kernels": {},
         "step_us_by_events": round(ms_events * 1e3, 2),
         "single_buffer_set": {"us_per_step_graph": round(one_ms * 1e3, 2),
-                              "GBps": round((d_bytes + c_bytes) / (one_ms * 1e-3) / 1e9, 1),
+                              "GBps": round((d_bytes + p_bytes + c_bytes) / (one_ms * 1e-3) / 1e9, 1),
                               "note": "one set of buffers reused every step: part of it stays in the MALL"},
         "eager_step": {"us_per_step": round(eager_ms * 1e3, 2),
-                       "GBps": round((d_bytes + c_bytes) / (eager_ms * 1e-3) / 1e9, 1)},
+                       "GBps": round((d_bytes + p_bytes + c_bytes) / (eager_ms * 1e-3) / 1e9, 1)},
     }
-    if llp is not None:
-        out["kernels"]["ll_dispatch"] = {"us": round(ld_ms * 1e3, 2), "bytes": d_bytes,
-                                         "GBps": round(d_bytes / (ld_ms * 1e-3) / 1e9, 1)}
-    elif len(per_op) == 2:
-        out["kernels"]["layout_dispatch"] = {"us": round(ld_ms * 1e3, 2), "bytes": d_bytes,
-                                             "GBps": round(d_bytes / (ld_ms * 1e-3) / 1e9, 1)}
-    else:
-        out["kernels"]["layout"] = {"us": round(lay_ms * 1e3, 2)}
-        out["kernels"]["dispatch"] = {"us": round(dis_ms * 1e3, 2), "bytes": d_bytes,
-                                      "GBps": round(d_bytes / (dis_ms * 1e-3) / 1e9, 1)}
-    out["kernels"]["combine"] = {"us": round(com_ms * 1e3, 2), "bytes": c_bytes, "GBps": round(achieved, 1)}
-    for kname, (p10, p50, p90) in zip(out["kernels"], op_stats):
+    if dedp is not None:
+        out["config"]["bytes"] = {"dispatch": d_bytes, "prereduce": p_bytes, "combine": c_bytes,
+                                  "note": "value counts all three: the pre-reduction is part of this step"}
+    op_bytes = {"layout_dispatch": d_bytes, "dispatch": d_bytes, "ll_dispatch": d_bytes, "prereduce": p_bytes}
+    for name, t_ms in op_ms.items():
+        if name == "combine":
+            out["kernels"]["combine"] = {"us": round(t_ms * 1e3, 2), "bytes": c_bytes, "GBps": round(achieved, 1)}
+        elif name == "layout":
+            out["kernels"]["layout"] = {"us": round(t_ms * 1e3, 2)}
+        else:
+            b_ = op_bytes[name]
+            out["kernels"][name] = {"us": round(t_ms * 1e3, 2), "bytes": b_,
+                                    "GBps": round(b_ / (t_ms * 1e-3) / 1e9, 1)}
+    for kname, (p10, p50, p90) in zip(op_names, op_stats):
         out["kernels"][kname].update({"p10_us": round(p10 * 1e3, 2), "median_us": round(p50 * 1e3, 2),
                                       "p90_us": round(p90 * 1e3, 2)})
     if not args.no_extras:
@@ -933,37 +1032,56 @@ def main():
                              "GBps": round(2 * nb / (copy_ms * 1e-3) / 1e9, 1)}
     del src, dst
     if not args.no_extras:
-        # rank-deduplicated exchange on the same inputs: one row per
-        # (token, destination rank), combine of the pre-reduced rows
-        dp = DedupPath(main_path, torch, ep, workloads, args.seed)
-        ops = [dp.layout_op, dp.dispatch_op, dp.combine_op]
-        e_ms, (l_, d_, c_) = timed(torch, ops, K, W)
-        g3_ms, _, _ = graph_step_timed(torch, ops, K, W)
-        fops = [dp.fused_op, dp.combine_op]
-        ef_ms, (ld_, _) = timed(torch, fops, K, W)
-        g_ms, _, _ = graph_step_timed(torch, fops, K, W)
-        if dp.buf.status():
-            raise SystemExit(f"bench: device status {dp.buf.status()} on {cfg.name} (dedup)")
-        Nd = dp.rows()
-        dd, dc = dedup_bytes(cfg.T, cfg.k, cfg.H, Nd, cfg.use_fp8)
-        out["dedup"] = {"workload": cfg.name, "rows": Nd, "rows_per_expert_path": N, "cap_rows": dp.cap,
-                        "us_per_step_graph": round(g_ms * 1e3, 2), "us_per_step_eager": round(ef_ms * 1e3, 2),
-                        "layout_dispatch_us": round(ld_ * 1e3, 2),
-                        "three_calls": {"us_per_step_graph": round(g3_ms * 1e3, 2),
-                                        "us_per_step_eager": round(e_ms * 1e3, 2)},
-                        "layout_us": round(l_ * 1e3, 2),
-                        "dispatch": {"us": round(d_ * 1e3, 2), "bytes": dd,
-                                     "GBps": round(dd / (d_ * 1e-3) / 1e9, 1),
-                                     "frac": round(dd / (d_ * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        # rank-deduplicated exchange on the same inputs, over rotated sets as
+        # the main step: one row per (token, destination rank), the
+        # expert-side pre-reduction of each row's expert outputs, and the
+        # combine of the reduced rows. Like for like, this step takes x to
+        # the combined tokens as the per-expert step does; its exchange alone
+        # (the two launches that cross ranks across GPUs) is timed beside it.
+        dq = [main_path] + [Path(cfg, args.seed + i, torch, ep, workloads) for i in range(1, n_sets)]
+        dps = [DedupPath(q, torch, ep, workloads, args.seed + i) for i, q in enumerate(dq)]
+        full = [[f.fused_op, f.prereduce_op, f.combine_op] for f in dps]
+        g_ms = graph_rotating(torch, full, K, W)[0]
+        ex_ms = graph_rotating(torch, [[f.fused_op, f.combine_op] for f in dps], K, W)[0]
+        e_ms, (ld_, pr_, c_) = timed_rotating(torch, full, K, W)
+        g4_ms = graph_rotating(torch, [[f.layout_op, f.dispatch_op, f.prereduce_op, f.combine_op] for f in dps],
+                               K, W)[0]
+        for f in dps:
+            if f.buf.status():
+                raise SystemExit(f"bench: device status {f.buf.status()} on {cfg.name} (dedup)")
+        Nd = dps[0].rows()
+        dd, dpre, dc = dedup_bytes(cfg.T, cfg.k, cfg.H, Nd, N, cfg.use_fp8)
+        out["dedup"] = {"workload": cfg.name, "rows": Nd, "rows_per_expert_path": N, "cap_rows": dps[0].cap,
+                        "rotated_sets": len(dps),
+                        "step": "fused deduplicated layout+dispatch, expert-side pre-reduction, combine of the "
+                                "reduced rows (HIP graph)",
+                        "us_per_step_graph": round(g_ms * 1e3, 2), "bytes": dd + dpre + dc,
+                        "GBps_graph": round((dd + dpre + dc) / (g_ms * 1e-3) / 1e9, 1),
+                        "per_expert_step_us": round(ms * 1e3, 2),
+                        "time_vs_per_expert_step": round(g_ms / ms, 3),
+                        "four_launches_us_per_step_graph": round(g4_ms * 1e3, 2),
+                        "us_per_step_eager": round(e_ms * 1e3, 2),
+                        "exchange_only": {"us_per_step_graph": round(ex_ms * 1e3, 2), "bytes": dd + dc,
+                                          "time_vs_per_expert_step": round(ex_ms / ms, 3),
+                                          "note": "fused dispatch + combine: what crosses ranks across GPUs; "
+                                                  "one GPU's HBM also carries the pre-reduction"},
+                        "layout_dispatch": {"us": round(ld_ * 1e3, 2), "bytes": dd,
+                                            "GBps": round(dd / (ld_ * 1e-3) / 1e9, 1),
+                                            "frac": round(dd / (ld_ * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+                        "prereduce": {"us": round(pr_ * 1e3, 2), "bytes": dpre,
+                                      "GBps": round(dpre / (pr_ * 1e-3) / 1e9, 1),
+                                      "frac": round(dpre / (pr_ * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
                         "combine": {"us": round(c_ * 1e3, 2), "bytes": dc,
                                     "GBps": round(dc / (c_ * 1e-3) / 1e9, 1),
-                                    "frac": round(dc / (c_ * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
-                        "GBps_graph": round((dd + dc) / (g_ms * 1e-3) / 1e9, 1),
-                        "speedup_vs_per_expert_step": round(ms / g_ms, 3)}
-        print(f"# dedup: {g_ms * 1e3:.1f} us/step graph fused ({g3_ms * 1e3:.1f} three calls), rows {Nd} of {N}",
-              file=sys.stderr, flush=True)
-        dp.buf.close()
-        del dp
+                                    "frac": round(dc / (c_ * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}}
+        print(f"# dedup: {g_ms * 1e3:.1f} us/step with pre-reduction ({ex_ms * 1e3:.1f} exchange only), "
+              f"rows {Nd} of {N}", file=sys.stderr, flush=True)
+        for f in dps:
+            f.buf.close()
+        for q in dq[1:]:
+            q.buf.close()
+        del dps, dq, full
+        torch.cuda.empty_cache()
 
     if not args.no_extras and cfg.T // cfg.R <= 256:
         # the low-latency form at this shape: same rows and bytes, fixed
