@@ -95,7 +95,8 @@ hipError_t launch_layout_dispatch(const LayoutArgs &la, const DispatchArgs &da, 
                                   int resident_blocks, hipStream_t s);
 int layout_dispatch_blocks_per_cu(int k, bool fp8, int mode, size_t lds);
 // prereduce: a.pos holds the received rows' routing entries and a.rows the
-// per-(row, slot) expert outputs (see CombineArgs)
+// per-(row, slot) expert outputs (see CombineArgs); its own kernel, which
+// sizes its grid itself (num_waves is not used)
 hipError_t launch_combine(const CombineArgs &a, bool out_f32, bool prereduce, int num_waves, hipStream_t s);
 hipError_t launch_copy(const void *src, void *dst, size_t n16, hipStream_t s);
 hipError_t launch_cu_census(int blocks, int naps, uint32_t *ids, hipStream_t s);

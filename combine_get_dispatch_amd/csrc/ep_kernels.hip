@@ -1445,30 +1445,19 @@ __global__ __launch_bounds__(kTileTokens) void k_layout_dispatch(LayoutArgs la, 
 
 constexpr int kSlotChunk = 8;
 
-// PREREDUCE: the expert-side pre-reduction of rank-deduplicated rows, the
-// same arithmetic over other indices. "Token" t is received row p of rank
-// d = p / cap_rows (the wave ends if p is past token_rows[d]); its slot j is
-// read when the row's routing entry pos[p][j] (the local expert) is >= 0,
-// from row p*k + j of the per-(row, slot) expert outputs.
-template <bool OUT_F32, bool PREREDUCE>
+template <bool OUT_F32>
 __global__ __launch_bounds__(kWavesPerBlock * 64) void k_combine(CombineArgs a) {
     const int lane = threadIdx.x & 63;
     const int gw = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
     const int t = gw / a.waves_per_token;
     const int part = gw - t * a.waves_per_token;
     if (t >= a.T) return;
-    if (PREREDUCE) {
-        const int64_t d = t / a.cap_rows;
-        if (t - d * a.cap_rows >= (int64_t)a.token_rows[d]) return;  // not a used row (whole wave)
-    }
 
     int p = -1;
     float wt = 1.0f;
     if (lane < a.k) {
         p = a.pos[(size_t)t * a.k + lane];
-        if (PREREDUCE) {
-            p = p >= 0 ? t * a.k + lane : -1;
-        } else if (p < -1 || p >= a.num_rows) {  // not a position this buffer holds
+        if (p < -1 || p >= a.num_rows) {  // not a position this buffer holds
             atomicOr(a.status, kStBadHandle);
             p = -1;
         }
@@ -1565,6 +1554,118 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void k_combine(CombineArgs a) 
                                  bf16_rne(acc1[6]) | (bf16_rne(acc1[7]) << 16)};
                 __builtin_nontemporal_store(o, reinterpret_cast<u32x4 *>(out + 512));
             }
+        }
+    }
+}
+
+// Expert-side pre-reduction of rank-deduplicated rows, M consecutive
+// received rows per wave (one 1024-channel pass of each): lanes l < M*k load
+// the routing entry of row r0 + l/k, slot l%k, and whether that row is used
+// (row p of rank d = p / cap_rows is used below token_rows[d]); a ballot gives
+// the valid (row, slot) pairs in row-major slot order, whose expert outputs
+// (entry p*k + j of the per-(row, slot) outputs) are loaded C at a time
+// through buffer resources and summed per row with one fused multiply-add per
+// slot in slot order, then rounded to bf16 (or kept fp32) and written for the
+// used rows. One routing round trip serves M rows, so a wave keeps M times
+// the bytes of a one-row wave in flight.
+template <bool OUT_F32, int M, int C>
+__global__ __launch_bounds__(kWavesPerBlock * 64) void k_prereduce(CombineArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int gw = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+    const int grp = gw / a.npass, ps = gw - grp * a.npass;
+    const int r0 = grp * M;
+    if (r0 >= a.T) return;  // whole wave
+    const int k = a.k, H = a.H;
+    const int lr = lane / k, ls = lane - lr * k;
+    const int row = r0 + lr;
+    const bool mine = lr < M && row < a.T;
+    // the row's used flag and its routing entry, loaded together
+    const int rc = mine ? row : r0;
+    const int d = (int)(rc / a.cap_rows);
+    const int tr = a.token_rows[d];
+    const int e = a.pos[(size_t)rc * k + (mine ? ls : 0)];
+    const float wt = (a.w && mine) ? a.w[(size_t)rc * k + ls] : 1.0f;
+    const bool used = mine && (int64_t)rc - (int64_t)d * a.cap_rows < (int64_t)tr;
+    const uint64_t valid = __ballot(used && e >= 0);
+    const uint64_t used_lanes = __ballot(used && ls == 0);
+    const int c0 = ps * 1024 + lane * 8;  // channels c0..c0+7 and c0+512..c0+519
+    float acc[M][16];
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[m][i] = 0.0f;
+    uint64_t rem = valid;
+    while (rem) {  // wave-uniform
+        int pl[C];
+        u32x4 v0[C], v1[C];
+#pragma unroll
+        for (int q = 0; q < C; ++q) {
+            pl[q] = rem ? __builtin_ctzll(rem) : -1;
+            rem &= rem - 1;  // (0 stays 0)
+            const int ll = max(pl[q], 0);
+            const int rr = r0 + ll / k, ss = ll - (ll / k) * k;
+            const __amdgpu_buffer_rsrc_t src = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<uint16_t *>(a.rows + ((size_t)rr * k + ss) * H), 0, pl[q] >= 0 ? H * 2 : 0,
+                kBufferRsrcWord3);
+            v0[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(src, c0 * 2, 0, kLoadNonTemporal));
+            v1[q] = __builtin_bit_cast(u32x4,
+                                       __builtin_amdgcn_raw_buffer_load_b128(src, c0 * 2 + 1024, 0, kLoadNonTemporal));
+        }
+#pragma unroll
+        for (int q = 0; q < C; ++q) {
+            if (pl[q] < 0) continue;  // uniform
+            const float w = readlane_f(wt, pl[q]);
+            const int m = pl[q] / k;
+            const u32x4 u = v0[q], z = v1[q];
+            const float f[16] = {bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y),
+                                 bf16_lo(u.z), bf16_hi(u.z), bf16_lo(u.w), bf16_hi(u.w),
+                                 bf16_lo(z.x), bf16_hi(z.x), bf16_lo(z.y), bf16_hi(z.y),
+                                 bf16_lo(z.z), bf16_hi(z.z), bf16_lo(z.w), bf16_hi(z.w)};
+#pragma unroll
+            for (int mm = 0; mm < M; ++mm) {
+                if (mm != m) continue;  // uniform
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc[mm][i] = __builtin_fmaf(w, f[i], acc[mm][i]);
+            }
+        }
+    }
+    const bool a0 = c0 < H, a1 = c0 + 512 < H;
+#pragma unroll
+    for (int mm = 0; mm < M; ++mm) {
+        if (!((used_lanes >> (mm * k)) & 1)) continue;  // row not used (uniform)
+        const size_t base = (size_t)(r0 + mm) * H + c0;
+        if (OUT_F32) {
+            float *out = static_cast<float *>(a.out) + base;
+            if (a0) {
+                reinterpret_cast<u32x4 *>(out)[0] = u32x4{__float_as_uint(acc[mm][0]), __float_as_uint(acc[mm][1]),
+                                                          __float_as_uint(acc[mm][2]), __float_as_uint(acc[mm][3])};
+                reinterpret_cast<u32x4 *>(out)[1] = u32x4{__float_as_uint(acc[mm][4]), __float_as_uint(acc[mm][5]),
+                                                          __float_as_uint(acc[mm][6]), __float_as_uint(acc[mm][7])};
+            }
+            if (a1) {
+                reinterpret_cast<u32x4 *>(out + 512)[0] =
+                    u32x4{__float_as_uint(acc[mm][8]), __float_as_uint(acc[mm][9]), __float_as_uint(acc[mm][10]),
+                          __float_as_uint(acc[mm][11])};
+                reinterpret_cast<u32x4 *>(out + 512)[1] =
+                    u32x4{__float_as_uint(acc[mm][12]), __float_as_uint(acc[mm][13]), __float_as_uint(acc[mm][14]),
+                          __float_as_uint(acc[mm][15])};
+            }
+        } else {
+            uint16_t *out = static_cast<uint16_t *>(a.out) + base;
+            if (a0)
+                __builtin_nontemporal_store(
+                    u32x4{bf16_rne(acc[mm][0]) | (bf16_rne(acc[mm][1]) << 16),
+                          bf16_rne(acc[mm][2]) | (bf16_rne(acc[mm][3]) << 16),
+                          bf16_rne(acc[mm][4]) | (bf16_rne(acc[mm][5]) << 16),
+                          bf16_rne(acc[mm][6]) | (bf16_rne(acc[mm][7]) << 16)},
+                    reinterpret_cast<u32x4 *>(out));
+            if (a1)
+                __builtin_nontemporal_store(
+                    u32x4{bf16_rne(acc[mm][8]) | (bf16_rne(acc[mm][9]) << 16),
+                          bf16_rne(acc[mm][10]) | (bf16_rne(acc[mm][11]) << 16),
+                          bf16_rne(acc[mm][12]) | (bf16_rne(acc[mm][13]) << 16),
+                          bf16_rne(acc[mm][14]) | (bf16_rne(acc[mm][15]) << 16)},
+                    reinterpret_cast<u32x4 *>(out + 512));
         }
     }
 }
@@ -1701,10 +1802,24 @@ hipError_t launch_dispatch(const DispatchArgs &a, bool fp8, int mode, int num_wa
 }
 
 hipError_t launch_combine(const CombineArgs &a, bool out_f32, bool prereduce, int num_waves, hipStream_t s) {
+    if (prereduce) {
+        // M received rows per wave (M * k lanes hold their routing entries),
+        // expert outputs loaded C pairs at a time. At 4096 tokens x 7168,
+        // top-8, 32 ranks (28153 rows) on MI355X: M = 4, C = 8 146.5 us;
+        // C = 4 149.2; M = 2 154.1; M = 8 169.2; M = 1 246.0 (same GPU).
+        constexpr int kPreM = 4, kPreC = 8;
+        const int m = a.k <= 16 ? 4 : a.k <= 32 ? 2 : 1;
+        const int waves = (int)((a.T + m - 1) / m) * a.npass;
+        const dim3 grid((waves + kWavesPerBlock - 1) / kWavesPerBlock), block(kWavesPerBlock * 64);
+        void (*fn)(CombineArgs) =
+            m == kPreM ? (out_f32 ? k_prereduce<true, kPreM, kPreC> : k_prereduce<false, kPreM, kPreC>)
+            : m == 2   ? (out_f32 ? k_prereduce<true, 2, kPreC> : k_prereduce<false, 2, kPreC>)
+                       : (out_f32 ? k_prereduce<true, 1, kPreC> : k_prereduce<false, 1, kPreC>);
+        hipLaunchKernelGGL(fn, grid, block, 0, s, a);
+        return hipGetLastError();
+    }
     const dim3 grid((num_waves + kWavesPerBlock - 1) / kWavesPerBlock), block(kWavesPerBlock * 64);
-    static void (*const kernels[4])(CombineArgs) = {k_combine<false, false>, k_combine<true, false>,
-                                                     k_combine<false, true>, k_combine<true, true>};
-    hipLaunchKernelGGL(kernels[(out_f32 ? 1 : 0) + (prereduce ? 2 : 0)], grid, block, 0, s, a);
+    hipLaunchKernelGGL(out_f32 ? k_combine<true> : k_combine<false>, grid, block, 0, s, a);
     return hipGetLastError();
 }
 
