@@ -79,7 +79,11 @@ __device__ __forceinline__ uint64_t pack_state(uint32_t epoch, uint64_t flag, ui
     return ((uint64_t)epoch << 34) | (flag << 32) | (uint64_t)v;
 }
 
-constexpr int kLookbackWindow = 32;  // predecessor states read per round trip
+// Predecessor states read per round trip. Eight keep the layout kernels at
+// 96 VGPRs and measured fastest on MI355X (same GPU, interleaved runs):
+// standalone layout at 4096 tokens 13.7 us vs 14.4 (16 states) and 16.8
+// (32); 16384 tokens as two launches 453.5 vs 458.4 us (32 states).
+constexpr int kLookbackWindow = 8;
 constexpr int kTileWaves = 4;
 constexpr int kTileTokens = kTileWaves * 64;
 
@@ -1391,9 +1395,13 @@ __device__ __forceinline__ LayoutWait make_wait(const LayoutArgs &la, uint32_t e
 // dispatch block has to wait for a free slot (it would then run its chain of
 // dependent loads behind everyone's row traffic). Not with a ticket: then
 // the layout blocks themselves need the slots their predecessors free.
+// Top-8 grids are held to 5 waves per SIMD (at most 102 VGPRs; 96 with the
+// 8-state look-back, no spills), so the whole prefill grid is resident at
+// once: 62.1 vs 63.3 us at 4096 tokens x 7168 top-8 with 4 waves per SIMD
+// (same GPU, interleaved runs). Wider top-k keeps its registers.
 template <int KMAX, bool FP8, int MODE>
-__global__ __launch_bounds__(kTileTokens) void k_layout_dispatch(LayoutArgs la, DispatchArgs da, int lgrid,
-                                                                 int extra) {
+__global__ __launch_bounds__(kTileTokens) __attribute__((amdgpu_waves_per_eu(KMAX <= 8 ? 5 : 1, 8))) void
+k_layout_dispatch(LayoutArgs la, DispatchArgs da, int lgrid, int extra) {
     // per expert: ranks and expert offsets (the totals); per rank: leader rows only
     constexpr bool kTotals = MODE == kRowsPerExpert;
     const int b = (int)blockIdx.x;
