@@ -135,6 +135,11 @@ int check_handle(const ep_ctx *ctx, const ep_handle *h) {
     return EP_OK;
 }
 
+// compute units the context's launches may use (its budget, else the device's)
+int usable_cus(const ep_ctx *ctx) {
+    return ctx->cu_budget > 0 ? std::min(ctx->cu_budget, ctx->cu_count) : ctx->cu_count;
+}
+
 int combine_common(ep_ctx *ctx, const uint16_t *rows, const ep_handle *h, const float *w, void *out,
                    bool out_f32, ep_stream_t stream, const char *name) {
     if (!ctx) return EP_ERR_ARG;
@@ -162,7 +167,9 @@ int combine_common(ep_ctx *ctx, const uint16_t *rows, const ep_handle *h, const 
     if (ctx->debug)
         std::fprintf(stderr, "libep: %s T=%d k=%d H=%d waves=%d (%d/token, %d passes each)\n", name, a.T, a.k,
                      a.H, g.num_waves, g.wpt, g.ppw);
-    return hip_fail(ep::launch_combine(a, out_f32, false, g.num_waves, (hipStream_t)stream), name);
+    // the residency cap is measured for a stream that has every CU
+    const int cap_cus = ctx->cu_budget > 0 && ctx->cu_budget < ctx->cu_count ? 0 : ctx->cu_count;
+    return hip_fail(ep::launch_combine(a, out_f32, false, g.num_waves, cap_cus, (hipStream_t)stream), name);
 }
 
 // The expert-side pre-reduction of deduplicated rows: the combine kernel over
@@ -201,7 +208,7 @@ int prereduce_common(ep_ctx *ctx, const uint16_t *expert_out, const int32_t *rec
     if (ctx->debug)
         std::fprintf(stderr, "libep: %s rows=%lld k=%d H=%d waves=%d\n", name, (long long)rows, a.k, a.H,
                      g.num_waves);
-    return hip_fail(ep::launch_combine(a, out_f32, true, g.num_waves, (hipStream_t)stream), name);
+    return hip_fail(ep::launch_combine(a, out_f32, true, g.num_waves, 0, (hipStream_t)stream), name);
 }
 
 // log2(v) when v is a power of two, else -1
@@ -335,7 +342,7 @@ int launch_fused(ep_ctx *ctx, const ep::LayoutArgs &la, const ep::DispatchArgs &
     if (per_cu < 0)
         per_cu = ep::layout_dispatch_blocks_per_cu(c.num_topk, fp8, mode,
                                                    ep::layout_lds_bytes(c.num_experts + c.num_ranks));
-    const int cus = ctx->cu_budget > 0 ? std::min(ctx->cu_budget, ctx->cu_count) : ctx->cu_count;
+    const int cus = usable_cus(ctx);
     return hip_fail(ep::launch_layout_dispatch(la, da, fp8, mode, num_waves, cus * per_cu, (hipStream_t)stream),
                     name);
 }

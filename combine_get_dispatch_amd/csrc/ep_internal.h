@@ -96,8 +96,10 @@ hipError_t launch_layout_dispatch(const LayoutArgs &la, const DispatchArgs &da, 
 int layout_dispatch_blocks_per_cu(int k, bool fp8, int mode, size_t lds);
 // prereduce: a.pos holds the received rows' routing entries and a.rows the
 // per-(row, slot) expert outputs (see CombineArgs); its own kernel, which
-// sizes its grid itself (num_waves is not used)
-hipError_t launch_combine(const CombineArgs &a, bool out_f32, bool prereduce, int num_waves, hipStream_t s);
+// sizes its grid itself (num_waves is not used). cus: the device's compute
+// units when the stream may use all of them, else 0 (no residency cap).
+hipError_t launch_combine(const CombineArgs &a, bool out_f32, bool prereduce, int num_waves, int cus,
+                          hipStream_t s);
 hipError_t launch_copy(const void *src, void *dst, size_t n16, hipStream_t s);
 hipError_t launch_cu_census(int blocks, int naps, uint32_t *ids, hipStream_t s);
 // low-latency dispatch: a.T % R == 0, a.T / R <= kLayoutTile, rows e*T + s*(T/R) + r
