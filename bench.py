@@ -526,7 +526,7 @@ KERNELS = {  # regular expressions on the kernel names rocprofv3 reports
     "k_layout": r"k_layout<", "k_layout_dispatch": r"k_layout_dispatch<\d+, \w+, 1>",
     "k_layout_dispatch_dedup": r"k_layout_dispatch<\d+, \w+, 2>", "k_dispatch": r"k_dispatch<true, 1(, \w+)?>",
     "k_dispatch_dedup": r"k_dispatch<true, 2(, \w+)?>", "k_ll_dispatch": r"k_ll_dispatch<",
-    "k_combine": r"k_combine<false>", "k_prereduce": r"k_prereduce<false", "k_copy": r"k_copy"}
+    "k_combine": r"k_combine<false,", "k_prereduce": r"k_prereduce<false", "k_copy": r"k_copy"}
 
 
 def _csv_rows(d, suffix):
@@ -558,13 +558,14 @@ COUNTER_PASSES = [
     "TCC_EA0_WRREQ_sum TCC_EA0_WRREQ_LEVEL_sum TCC_EA0_WRREQ_DRAM_CREDIT_STALL_sum TCC_EA0_WRREQ_STALL_sum",
     "TCC_EA0_WRREQ_64B_sum TCC_TOO_MANY_EA_WRREQS_STALL_sum TCC_EA0_RDREQ_128B_sum TCC_EA0_RDREQ_64B_sum",
 ]
-# waves per SIMD the code objects allow (VGPRs), for the occupancy bound
-# (compiler resource-usage remarks of this build: k_layout<8> and the top-8 fused
-# grids 113 VGPRs, the FP8 per-expert dispatch 91, the per-rank one 99, the
-# combine 92, the four-row pre-reduction 143, the one-pass top-8 FP8
-# low-latency dispatch 56, the copy 10)
+# waves per SIMD the code objects allow (VGPRs; for the combine of a long
+# launch, the LDS each two-wave workgroup reserves: 4 per CU), for the
+# occupancy bound (compiler resource-usage remarks of this build: k_layout<8>
+# and the top-8 fused grids 113 VGPRs, the FP8 per-expert dispatch 91, the
+# per-rank one 99, the combine 92, the four-row pre-reduction 143, the
+# one-pass top-8 FP8 low-latency dispatch 56, the copy 10)
 WAVES_PER_SIMD_BOUND = {"k_layout": 4, "k_layout_dispatch": 4, "k_layout_dispatch_dedup": 4, "k_dispatch": 5,
-                        "k_dispatch_dedup": 4, "k_ll_dispatch": 8, "k_combine": 5, "k_prereduce": 3, "k_copy": 8}
+                        "k_dispatch_dedup": 4, "k_ll_dispatch": 8, "k_combine": 2, "k_prereduce": 3, "k_copy": 8}
 
 
 def record_counters(args, cfg):

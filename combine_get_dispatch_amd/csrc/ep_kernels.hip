@@ -1452,13 +1452,13 @@ k_layout_dispatch(LayoutArgs la, DispatchArgs da, int lgrid, int extra) {
 // ---------------------------------------------------------------------------
 
 constexpr int kSlotChunk = 8;
-constexpr size_t kCombineCapLds = 64 * 1024;  // 2 workgroups in a CU's 160 KB of LDS
-constexpr int kCombineCapMinBlocksPerCu = 16;
+constexpr size_t kCombineCapLds = 40 * 1024;  // 4 two-wave workgroups in a CU's 160 KB of LDS
+constexpr int kCombineCapMinWavesPerCu = 64;
 
-template <bool OUT_F32>
-__global__ __launch_bounds__(kWavesPerBlock * 64) void k_combine(CombineArgs a) {
+template <bool OUT_F32, int WPB>
+__global__ __launch_bounds__(WPB * 64) void k_combine(CombineArgs a) {
     const int lane = threadIdx.x & 63;
-    const int gw = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+    const int gw = blockIdx.x * WPB + (threadIdx.x >> 6);
     const int t = gw / a.waves_per_token;
     const int part = gw - t * a.waves_per_token;
     if (t >= a.T) return;
@@ -1829,18 +1829,25 @@ hipError_t launch_combine(const CombineArgs &a, bool out_f32, bool prereduce, in
         hipLaunchKernelGGL(fn, grid, block, 0, s, a);
         return hipGetLastError();
     }
-    const dim3 grid((num_waves + kWavesPerBlock - 1) / kWavesPerBlock), block(kWavesPerBlock * 64);
-    // A long combine runs at most two workgroups (8 waves) per CU: each
-    // workgroup reserves LDS it does not use, so that fewer tokens' rows are
+    // A long combine runs at most 8 waves per CU, in two-wave workgroups
+    // that each reserve LDS they do not use, so that fewer tokens' rows are
     // read at once. Those reads then fall in a narrower window of the expert
     // outputs, which the DRAM serves faster. Measured on MI355X, 4096 tokens
-    // x 7168 top-8 (28 workgroups per CU): 88.2-89.8 us against 91.2-91.5
-    // uncapped, prefill step 150.7 against 153.8 us; 16384 tokens (BF16):
-    // 348.8 against 375.8 us; three workgroups per CU gain less. Shorter
-    // combines lose by it (1024 tokens: 24.9 against 23.4 us; 2048: 46.3
-    // against 45.6), so the cap starts at 16 workgroups per CU.
-    const size_t lds = cus > 0 && grid.x >= (unsigned)(kCombineCapMinBlocksPerCu * cus) ? kCombineCapLds : 0;
-    hipLaunchKernelGGL(out_f32 ? k_combine<true> : k_combine<false>, grid, block, lds, s, a);
+    // x 7168 top-8 (112 waves per CU): 88.2-89.8 us with four-wave
+    // workgroups, 2 per CU, against 91.2-91.5 us uncapped (prefill step 150.7
+    // against 153.8 us), and 88.0 against 89.1 us with two-wave workgroups;
+    // 16384 tokens (BF16): 348.8-352.2 against 375.8 us. 4, 6 and 12 waves
+    // per CU gain less or lose. Shorter combines lose by the cap (1024
+    // tokens: 24.9 against 23.4 us; 2048: 46.3 against 45.6), so it starts
+    // at 64 waves per CU.
+    if (cus > 0 && num_waves >= kCombineCapMinWavesPerCu * cus) {
+        const dim3 grid((num_waves + 1) / 2), block(2 * 64);
+        hipLaunchKernelGGL((out_f32 ? k_combine<true, 2> : k_combine<false, 2>), grid, block, kCombineCapLds, s, a);
+        return hipGetLastError();
+    }
+    const dim3 grid((num_waves + kWavesPerBlock - 1) / kWavesPerBlock), block(kWavesPerBlock * 64);
+    hipLaunchKernelGGL((out_f32 ? k_combine<true, kWavesPerBlock> : k_combine<false, kWavesPerBlock>), grid, block,
+                       0, s, a);
     return hipGetLastError();
 }
 
