@@ -495,6 +495,57 @@ def graph_timed(torch, ops, K, W, inner=20):
     return e0.elapsed_time(e1) * 1e3 / n, wall * 1e6 / n
 
 
+def pattern_floors(torch, ep, steps, sets, K, W, d_bytes, c_bytes, N):
+    """The step's memory-access patterns with none of its arithmetic (the
+    ep_pattern_* utilities), each timed like the dominant kernel (K launches
+    back to back over the rotated sets), beside the fused launch and the
+    combine timed the same way: the rate the HBM sustains for the pattern a
+    kernel must make, against which its own rate is compared.
+      push    x row read, then k scattered FP8-sized row writes per token
+      gather  k scattered row reads, then one row write per token (at the
+              combine's residency cap, and uncapped)
+      fill    compact writes of the dispatch's row bytes
+      read    compact reads of the combine's row bytes"""
+    cfg = sets[0].cfg
+    T, k, H = cfg.T, cfg.k, cfg.H
+    nrows = sets[0].buf.num_rows
+    strm = lambda: torch.cuda.current_stream().cuda_stream
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    ms = lambda ops: back_to_back_rotating(torch, ops, K, W)
+    out = {"timing": f"{K} launches back to back between two HIP events, cycling through the {len(sets)} "
+                     "rotated sets (as the dominant kernel)"}
+    fused_ms = ms([st[0][0] for st in steps])
+    comb_ms = ms([st[0][-1] for st in steps])
+    gath_ms = ms([lambda q=q: ep.ep_pattern_gather(q.expert_out.data_ptr(), q.handle.pos.data_ptr(), q.y.data_ptr(),
+                                                   T, k, H, nrows, True, strm()) for q in sets])
+    gath_u_ms = ms([lambda q=q: ep.ep_pattern_gather(q.expert_out.data_ptr(), q.handle.pos.data_ptr(),
+                                                     q.y.data_ptr(), T, k, H, nrows, False, strm()) for q in sets])
+    r_bytes = (2 * N * H) // 4096 * 4096
+    read_ms = ms([lambda q=q: ep.ep_pattern_read(q.expert_out.data_ptr(), r_bytes, sink.data_ptr(), strm())
+                  for q in sets])
+    g_bytes = 2 * N * H + 2 * T * H
+    out["combine"] = {"us": round(comb_ms * 1e3, 2), "GBps": round(c_bytes / (comb_ms * 1e-3) / 1e9, 1)}
+    out["gather_capped"] = {"us": round(gath_ms * 1e3, 2), "bytes": g_bytes,
+                            "GBps": round(g_bytes / (gath_ms * 1e-3) / 1e9, 1)}
+    out["gather_uncapped"] = {"us": round(gath_u_ms * 1e3, 2), "GBps": round(g_bytes / (gath_u_ms * 1e-3) / 1e9, 1)}
+    out["read_compact"] = {"bytes": r_bytes, "GBps": round(r_bytes / (read_ms * 1e-3) / 1e9, 1)}
+    out["combine_rate_over_gather"] = round((c_bytes / comb_ms) / (g_bytes / gath_ms), 4)
+    out["layout_dispatch"] = {"us": round(fused_ms * 1e3, 2), "GBps": round(d_bytes / (fused_ms * 1e-3) / 1e9, 1)}
+    if cfg.use_fp8 and H <= 8192:
+        push_ms = ms([lambda q=q: ep.ep_pattern_push(q.x.data_ptr(), q.handle.pos.data_ptr(), q.recv_x.data_ptr(),
+                                                     T, k, H, nrows, strm()) for q in sets])
+        p_bytes = 2 * T * H + N * H
+        w_bytes = min(N * (H + H // 32), sets[0].recv_x.numel() * sets[0].recv_x.element_size()) // 1024 * 1024
+        fill_ms = ms([lambda q=q: ep.ep_pattern_fill(q.recv_x.data_ptr(), w_bytes, strm()) for q in sets])
+        out["push"] = {"us": round(push_ms * 1e3, 2), "bytes": p_bytes,
+                       "GBps": round(p_bytes / (push_ms * 1e-3) / 1e9, 1)}
+        out["fill_compact"] = {"bytes": w_bytes, "GBps": round(w_bytes / (fill_ms * 1e-3) / 1e9, 1)}
+        out["layout_dispatch_rate_over_push"] = round((d_bytes / fused_ms) / (p_bytes / push_ms), 4)
+        step_floor = d_bytes / (p_bytes / push_ms) + c_bytes / (g_bytes / gath_ms)
+        out["step_at_pattern_rates_us"] = round(step_floor * 1e3, 2)
+    return out
+
+
 def source_sha():
     h = hashlib.sha256()
     for f in ("ep_kernels.hip", "ep_api.hip", "ep_internal.h"):
@@ -986,6 +1037,13 @@ def main():
     print(f"# main: {ms * 1e3:.1f} us/step  " +
           "  ".join(f"{k} {v['us']:.1f}" for k, v in out["kernels"].items()) + " us", file=sys.stderr, flush=True)
 
+    if not args.no_extras and fused and not (args.ll or args.dedup) and cfg.H % 1024 == 0 and cfg.k <= 8:
+        pf = pattern_floors(torch, ep, steps, sets, K, W, d_bytes, c_bytes, N)
+        out["access_pattern_floors"] = pf
+        print(f"# access patterns: combine {pf['combine']['us']:.1f} us vs gather {pf['gather_capped']['us']:.1f}"
+              + (f"; layout+dispatch {pf['layout_dispatch']['us']:.1f} us vs push {pf['push']['us']:.1f}; "
+                 f"step at the patterns' rates {pf['step_at_pattern_rates_us']:.1f} us" if "push" in pf else ""),
+              file=sys.stderr, flush=True)
     for q, (_, b, f) in zip(sets, steps):
         if f is not q:
             b.close()

@@ -26,7 +26,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libep.so")
-SOURCES = [os.path.join(CSRC, "ep_kernels.hip"), os.path.join(CSRC, "ep_api.hip")]
+SOURCES = [os.path.join(CSRC, "ep_kernels.hip"), os.path.join(CSRC, "ep_api.hip"), os.path.join(CSRC, "ep_patterns.hip")]
 HEADERS = [os.path.join(CSRC, "ep_internal.h"), os.path.join(INCLUDE, "ep.h")]
 ARCH = "gfx950"
 

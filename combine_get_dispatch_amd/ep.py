@@ -107,6 +107,12 @@ SIGNATURES = {
     "ep_set_cu_budget": (ctypes.c_int, [c_void_p, ctypes.c_int]),
     "ep_set_spin_limit": (ctypes.c_int, [c_void_p, ctypes.c_uint32]),
     "ep_cu_census": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, c_void_p, c_void_p]),
+    "ep_pattern_fill": (ctypes.c_int, [c_void_p, ctypes.c_size_t, c_void_p]),
+    "ep_pattern_read": (ctypes.c_int, [c_void_p, ctypes.c_size_t, c_void_p, c_void_p]),
+    "ep_pattern_push": (ctypes.c_int, [c_void_p, c_void_p, c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_int64, c_void_p]),
+    "ep_pattern_gather": (ctypes.c_int, [c_void_p, c_void_p, c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_int64, ctypes.c_int, c_void_p]),
 }
 
 _lib = None
@@ -260,6 +266,25 @@ def ep_get_status(ctx: int, stream: int) -> int:
 
 def ep_copy_bytes(src: int, dst: int, nbytes: int, stream: int) -> None:
     _check(load().ep_copy_bytes(src, dst, nbytes, stream), "ep_copy_bytes")
+
+
+def ep_pattern_fill(dst: int, nbytes: int, stream: int) -> None:
+    _check(load().ep_pattern_fill(dst, nbytes, stream), "ep_pattern_fill")
+
+
+def ep_pattern_read(src: int, nbytes: int, sink: int, stream: int) -> None:
+    _check(load().ep_pattern_read(src, nbytes, sink, stream), "ep_pattern_read")
+
+
+def ep_pattern_push(x: int, pos: int, rows: int, num_tokens: int, num_topk: int, hidden: int, num_rows: int,
+                    stream: int) -> None:
+    _check(load().ep_pattern_push(x, pos, rows, num_tokens, num_topk, hidden, num_rows, stream), "ep_pattern_push")
+
+
+def ep_pattern_gather(rows: int, pos: int, out: int, num_tokens: int, num_topk: int, hidden: int, num_rows: int,
+                      capped: bool, stream: int) -> None:
+    _check(load().ep_pattern_gather(rows, pos, out, num_tokens, num_topk, hidden, num_rows, int(capped), stream),
+           "ep_pattern_gather")
 
 
 # ---------------------------------------------------------------------------

@@ -380,6 +380,34 @@ int ep_cu_census(int blocks, int naps, uint32_t *ids, ep_stream_t stream);
  * counters and as the attainable-bandwidth reference. */
 int ep_copy_bytes(const void *src, void *dst, size_t bytes, ep_stream_t stream);
 
+/* Measurement utilities: the memory-access patterns of the exchange with none
+ * of its arithmetic, layout or bookkeeping, timed beside the kernels as the
+ * rate the HBM sustains for each pattern. They write only the buffers given;
+ * the values they write are meaningless.
+ *  - ep_pattern_fill: compact writes of `bytes` (a multiple of 1024) to dst,
+ *    wave w storing bytes [1024w, 1024w + 1024).
+ *  - ep_pattern_read: compact reads of `bytes` (a multiple of 4096) of src,
+ *    4 KB per wave; sink (device, 1 uint32) is never written in practice.
+ *  - ep_pattern_push: the dispatch's pattern. One wave per token loads
+ *    x[t] (num_tokens x hidden bf16; hidden a multiple of 1024, at most 8192)
+ *    and stores `hidden` bytes (the high byte of each channel) to row
+ *    pos[t][j] of rows (num_rows x hidden bytes) for every slot with
+ *    0 <= pos[t][j] < num_rows (pos: num_tokens x num_topk int32, num_topk
+ *    at most 64).
+ *  - ep_pattern_gather: the combine's pattern. One wave per (token,
+ *    1024-channel pass) loads that pass of rows pos[t][j] of rows (num_rows
+ *    x hidden bf16; slots with 0 <= pos < num_rows; num_topk at most 8) and
+ *    stores their XOR to out[t] (num_tokens x hidden bf16); capped != 0
+ *    launches it at the combine's residency cap (8 waves per CU).
+ * Pointers to rows and vectors must be 16-byte aligned (EP_ERR_ALIGN);
+ * other sizes outside these bounds return EP_ERR_ARG. */
+int ep_pattern_fill(void *dst, size_t bytes, ep_stream_t stream);
+int ep_pattern_read(const void *src, size_t bytes, uint32_t *sink, ep_stream_t stream);
+int ep_pattern_push(const uint16_t *x, const int32_t *pos, void *rows, int num_tokens, int num_topk, int hidden,
+                    int64_t num_rows, ep_stream_t stream);
+int ep_pattern_gather(const uint16_t *rows, const int32_t *pos, uint16_t *out, int num_tokens, int num_topk,
+                      int hidden, int64_t num_rows, int capped, ep_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -95,6 +95,22 @@ def test_null_args_rejected_without_gpu(lib):
     assert L.ep_destroy(None) == ep.EP_OK
     assert L.ep_copy_bytes(None, None, 0, None) == ep.EP_OK
     assert L.ep_copy_bytes(None, None, 16, None) == ep.EP_ERR_ARG
+    # the access-pattern utilities: refusals without a launch
+    assert L.ep_pattern_fill(None, 0, None) == ep.EP_OK
+    assert L.ep_pattern_fill(None, 1024, None) == ep.EP_ERR_ARG
+    assert L.ep_pattern_fill(ctypes.c_void_p(16), 1000, None) == ep.EP_ERR_ARG
+    assert L.ep_pattern_fill(ctypes.c_void_p(8), 1024, None) == ep.EP_ERR_ALIGN
+    assert L.ep_pattern_read(ctypes.c_void_p(16), 4096, None, None) == ep.EP_ERR_ARG
+    assert L.ep_pattern_read(ctypes.c_void_p(16), 1024, ctypes.c_void_p(16), None) == ep.EP_ERR_ARG
+    p16 = ctypes.c_void_p(16)
+    assert L.ep_pattern_push(p16, p16, p16, 0, 8, 7168, 10, None) == ep.EP_OK
+    assert L.ep_pattern_push(p16, p16, p16, 4, 8, 7000, 10, None) == ep.EP_ERR_ARG   # hidden % 1024
+    assert L.ep_pattern_push(p16, p16, p16, 4, 8, 9216, 10, None) == ep.EP_ERR_ARG   # > 8192
+    assert L.ep_pattern_push(p16, p16, p16, 4, 65, 7168, 10, None) == ep.EP_ERR_ARG  # top-k > 64
+    assert L.ep_pattern_push(ctypes.c_void_p(8), p16, p16, 4, 8, 7168, 10, None) == ep.EP_ERR_ALIGN
+    assert L.ep_pattern_gather(p16, p16, p16, 4, 9, 7168, 10, 0, None) == ep.EP_ERR_ARG  # top-k > 8
+    assert L.ep_pattern_gather(p16, p16, None, 4, 8, 7168, 10, 0, None) == ep.EP_ERR_ARG
+    assert L.ep_pattern_gather(p16, p16, ctypes.c_void_p(8), 4, 8, 7168, 10, 1, None) == ep.EP_ERR_ALIGN
 
 
 def _xcd_counts(mask, cu_count, interleaved):
