@@ -647,9 +647,10 @@ def record_counters(args, cfg):
               "--record-counters " + " ".join(f"<pass{i + 1}>" for i in range(len(passes))), "",
               "Means over the profiled launches of each kernel. Occupancy: OccupancyPercent is the mean of "
               "resident waves over a CU's 32 wave slots (4 SIMDs x 8) while the kernel runs; the bound is what "
-              "the code object's VGPR count allows. Latencies are TCC (L2) cycles from a request leaving L2 to "
+              "the code object's VGPR count allows (for the combine of a long launch, the LDS its two-wave "
+              "workgroups reserve). Latencies are TCC (L2) cycles from a request leaving L2 to "
               "its return (LEVEL / REQ); credit stalls are cycles summed over the L2 channels.", "",
-              "| kernel | launches | occupancy % | waves/CU | VGPR bound waves/CU | read latency | write latency | "
+              "| kernel | launches | occupancy % | waves/CU | bound waves/CU | read latency | write latency | "
               "read credit stall / req | write credit stall / req | 128B reads % | 64B writes % |",
               "|---|---|---|---|---|---|---|---|---|---|---|"]
     for k, c in vals.items():
