@@ -615,6 +615,7 @@ COUNTER_PASSES = [
 # and the top-8 fused grids 113 VGPRs, the FP8 per-expert dispatch 91, the
 # per-rank one 99, the combine 92, the four-row pre-reduction 143, the
 # one-pass top-8 FP8 low-latency dispatch 56, the copy 10)
+COMBINE_CAP_MIN_WAVES = 64 * 256  # the combine runs capped from 64 waves per CU (256 CUs)
 WAVES_PER_SIMD_BOUND = {"k_layout": 4, "k_layout_dispatch": 4, "k_layout_dispatch_dedup": 4, "k_dispatch": 5,
                         "k_dispatch_dedup": 4, "k_ll_dispatch": 8, "k_combine": 2, "k_prereduce": 3, "k_copy": 8}
 
@@ -663,6 +664,8 @@ def record_counters(args, cfg):
         div = lambda a, b: None if a is None or not b else a / b
         nl = max(len(v) for v in c.values())
         bound = WAVES_PER_SIMD_BOUND.get(k)
+        if k == "k_combine" and cfg.T * -(-cfg.H // 1024) < COMBINE_CAP_MIN_WAVES:
+            bound = 5  # a short combine runs uncapped: its VGPRs (92) bound it
         lines.append(f"| `{k}` | {nl} | {f(occ, '{:.1f}')} | {f(None if occ is None else occ * 32 / 100, '{:.1f}')} | "
                      f"{f(None if bound is None else 4 * bound, '{:d}')} | {f(div(rdl, rd), '{:.0f}')} | "
                      f"{f(div(wrl, wr), '{:.0f}')} | {f(div(rds, rd), '{:.3f}')} | {f(div(wrs, wr), '{:.3f}')} | "
