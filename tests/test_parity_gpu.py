@@ -256,6 +256,12 @@ EDGE = {
     "one_tile_4_passes": dict(T=256, k=4, E=32, R=4, H=32768, fp8=True),
     "one_tile_8_passes": dict(T=256, k=2, E=16, R=4, H=65536, fp8=True),
     "one_tile_8_passes_bf16": dict(T=256, k=2, E=16, R=4, H=65536, fp8=False),
+    # combines long enough to run at the residency cap (at least 64 waves
+    # per CU of 256): an odd wave count (the last two-wave workgroup holds
+    # one wave past the tokens) with a partial last pass, and the FP8 prefill
+    # shape just above the threshold
+    "capped_combine_odd_waves_tail": dict(T=2347, k=8, E=64, R=8, H=7000, fp8=False),
+    "capped_combine_fp8": dict(T=2341, k=8, E=256, R=32, H=7168, fp8=True),
 }
 
 
