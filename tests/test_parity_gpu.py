@@ -260,8 +260,8 @@ EDGE = {
     # per CU of 256): an odd wave count (the last two-wave workgroup holds
     # one wave past the tokens) with a partial last pass, and the FP8 prefill
     # shape just above the threshold
-    "capped_combine_odd_waves_tail": dict(T=2347, k=8, E=64, R=8, H=7000, fp8=False),
-    "capped_combine_fp8": dict(T=2341, k=8, E=256, R=32, H=7168, fp8=True),
+    "capped_combine_odd_waves_tail": dict(T=2349, k=8, E=63, R=3, H=7000, fp8=False),
+    "capped_combine_fp8": dict(T=2368, k=8, E=256, R=32, H=7168, fp8=True),
 }
 
 
