@@ -19,7 +19,12 @@
 //               (all slots in flight, branch-free buffer loads, so each
 //               slot's arithmetic waits only for its own rows) and
 //               accumulates in fp32 with one fused
-//               multiply-add per slot in slot order, then rounds to bf16.
+//               multiply-add per slot in slot order, then rounds to bf16;
+//               a long launch runs at most 8 waves per CU (LDS reserved per
+//               workgroup), which narrows the window of rows read at once.
+//   k_prereduce expert-side pre-reduction of rank-deduplicated rows: several
+//               received rows per wave, each row's valid slots summed in
+//               slot order.
 //   k_copy      plain 128-bit streaming copy (bandwidth calibration).
 //   k_cu_census the compute unit each workgroup runs on (checks stream CU masks).
 //   k_ll_dispatch low-latency dispatch: fixed per-(expert, source) regions, no
