@@ -108,6 +108,11 @@ PRE_EDGE = {
     "bad_repeated_empty_slots": dict(T=300, k=6, E=48, R=6, H=1152, dirty=True),
     "channel_tail": dict(T=200, k=4, E=32, R=4, H=9224, fp8=False),
     "E1024_R64": dict(T=1024, k=8, E=1024, R=64, H=512),
+    # the rows per wave the launch picks from k: four rows at k = 16 (all 64
+    # lanes hold entries) and k = 3 (12 lanes), two rows at k = 17 (34 lanes)
+    "k16_four_rows_full_wave": dict(T=256, k=16, E=64, R=8, H=1024),
+    "k3_R3": dict(T=300, k=3, E=12, R=3, H=2048),
+    "k17_two_rows": dict(T=96, k=17, E=68, R=4, H=1024),
 }
 
 
