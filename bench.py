@@ -593,7 +593,7 @@ def _csv_rows(d, suffix):
 def _per_kernel(rows, value_key):
     """Dispatches per kernel of interest in launch order (the bench runs the
     warmup and timed steps of the main loop first, so the first instances of
-    k_combine<false> are the forward combine, not dispatch_backward)."""
+    k_combine<false, *> are the forward combine, not dispatch_backward)."""
     out = {k: [] for k in KERNELS}
     for r in sorted(rows, key=lambda r: int(r.get("Dispatch_Id", r.get("Correlation_Id", 0)))):
         for k, pat in KERNELS.items():
