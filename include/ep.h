@@ -276,7 +276,12 @@ int ep_dispatch_low_latency(ep_ctx *ctx, const uint16_t *x, const int32_t *topk_
  * pos[t][j] >= 0: acc = fmaf(w[t][j], expert_out[pos[t][j]][i], acc) (w = 1
  * when weights is NULL); combined_x[t][i] = bf16(acc), round to nearest even.
  * expert_out: [R*cap_rows][H] bf16; weights: [T][k] fp32 or NULL;
- * combined_x: [T][H] bf16. Pointers 16-byte aligned. */
+ * combined_x: [T][H] bf16. Pointers 16-byte aligned.
+ * A launch of at least 64 waves per CU (one wave per token and 1024
+ * channels), on a context with no CU budget below the device's, holds each
+ * of its workgroups to 40 KB of LDS it does not use, so that at most 8 of its
+ * waves share a CU: kernels running beside it on the same CUs find that much
+ * less LDS free. (The same holds for ep_dispatch_backward.) */
 int ep_combine(ep_ctx *ctx, const uint16_t *expert_out, const ep_handle *handle,
                const float *weights, uint16_t *combined_x, ep_stream_t stream);
 
