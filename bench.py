@@ -61,6 +61,12 @@ def parse():
     p.add_argument("--record-counters", nargs="+", metavar="PASS_DIR",
                    help="summarize rocprofv3 --pmc runs of this bench (one counter set per run, "
                         "--output-format csv; the sets of COUNTER_PASSES) into profiles/")
+    p.add_argument("--patterns-only", action="store_true",
+                   help="after the timed steps, run only the access-pattern leg and print its figures "
+                        "(a short run for a kernel trace of the pattern kernels)")
+    p.add_argument("--record-patterns", metavar="TRACE_DIR",
+                   help="summarize a rocprofv3 --kernel-trace --stats run of this bench with --patterns-only "
+                        "(--output-format csv) into profiles/")
     p.add_argument("--record-traffic", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "TRACE_DIR"),
                    help="summarize rocprofv3 runs of this bench (--pmc FETCH_SIZE, --pmc WRITE_SIZE, "
                         "--kernel-trace --stats, all with --output-format csv) into profiles/")
@@ -681,6 +687,71 @@ def record_counters(args, cfg):
     return path
 
 
+def pattern_bytes(cfg, N):
+    """Bytes each measured kernel of the access-pattern leg moves (as
+    pattern_floors counts them): the step's two kernels' algorithmic bytes and
+    the patterns' own."""
+    T, k, H = cfg.T, cfg.k, cfg.H
+    d, c, _ = algo_bytes(T, k, H, N, cfg.use_fp8)
+    return {"k_layout_dispatch": d, "k_combine": c, "k_pattern_push": 2 * T * H + N * H,
+            "k_pattern_gather": 2 * N * H + 2 * T * H, "k_pattern_fill": N * (H + H // 32) // 1024 * 1024,
+            "k_pattern_read": (2 * N * H) // 4096 * 4096}
+
+
+PATTERN_KERNELS = {  # rocprofv3 kernel names
+    "k_layout_dispatch": r"k_layout_dispatch<\d+, \w+, 1>", "k_combine": r"k_combine<false, 2>",
+    "k_pattern_push": r"k_pattern_push", "k_pattern_gather": r"k_pattern_gather<2>",
+    "k_pattern_gather_uncapped": r"k_pattern_gather<4>", "k_pattern_fill": r"k_pattern_fill",
+    "k_pattern_read": r"k_pattern_read", "k_copy": r"k_copy"}
+
+
+def record_patterns(args, cfg):
+    """Average durations (rocprofv3 --kernel-trace --stats) of the step's two
+    kernels and of the access-pattern kernels, and the rates they imply.
+    Writes profiles/<workload>_access_patterns.md."""
+    from combine_get_dispatch_amd import workloads as wlmod
+    wl = wlmod.make_workload(cfg, seed=args.seed, with_x=False)
+    N = int((wl.topk_idx >= 0).sum())
+    nb = pattern_bytes(cfg, N)
+    nb["k_pattern_gather_uncapped"] = nb["k_pattern_gather"]
+    stats = _csv_rows(args.record_patterns, "kernel_stats.csv")
+    rows = {}
+    for key, pat in PATTERN_KERNELS.items():
+        for r in stats:
+            if re.search(pat, r["Name"]):
+                rows[key] = (int(r["Calls"]), float(r["AverageNs"]) / 1e3)
+    cmd = f"python3 bench.py --config {cfg.name} --steps {args.steps} --warmup {args.warmup} --no-cpu-baseline " \
+          "--no-decode --no-extras --patterns-only"
+    lines = [f"# {cfg.name}: the step's kernels beside their access patterns (rocprofv3 kernel trace)", "",
+             f"Workload: {cfg.desc}.", "",
+             "Commands (run from /tmp with TMPDIR=/tmp; the bench runs from the repository root):", "",
+             f"    rocprofv3 --kernel-trace --stats --output-format csv -d <trace> -o run -- {cmd}",
+             f"    python3 bench.py --config {cfg.name} --steps {args.steps} --warmup {args.warmup} "
+             "--record-patterns <trace>", "",
+             "The pattern kernels (`ep_pattern_*`) make the step's memory accesses with none of its arithmetic: "
+             "push (x row read, then k scattered FP8-sized row writes per token), gather (k scattered row "
+             "reads, then one row write per token; capped as the combine, and uncapped), compact fill and "
+             "compact read. Average duration per launch over the whole run (its launches cycle through the "
+             "rotated sets); rate = the bytes each launch moves / average duration.", "",
+             "| kernel | calls | avg us | bytes per launch | TB/s |", "|---|---|---|---|---|"]
+    for key in PATTERN_KERNELS:
+        if key not in rows or key == "k_copy":
+            continue
+        calls, us = rows[key]
+        lines.append(f"| `{key}` | {calls} | {us:.2f} | {nb[key]} | {nb[key] / (us * 1e-6) / 1e12:.3f} |")
+    if "k_layout_dispatch" in rows and "k_pattern_push" in rows and "k_combine" in rows and \
+            "k_pattern_gather" in rows:
+        rd = (nb["k_layout_dispatch"] / rows["k_layout_dispatch"][1]) / (nb["k_pattern_push"] / rows["k_pattern_push"][1])
+        rc = (nb["k_combine"] / rows["k_combine"][1]) / (nb["k_pattern_gather"] / rows["k_pattern_gather"][1])
+        lines += ["", f"Fused layout+dispatch rate / push pattern rate: {rd:.3f}. "
+                      f"Combine rate / gather pattern rate: {rc:.3f}."]
+    lines += ["", f"Kernel sources: sha256 prefix {source_sha()} (ep_kernels.hip, ep_api.hip, ep_internal.h)."]
+    path = os.path.join(PROFILES, f"{cfg.name}_access_patterns.md")
+    with open(path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    return path
+
+
 def traffic_key(cfg, args):
     return cfg.name + ("_low_latency" if args.ll else "_dedup" if args.dedup else "") + \
         ("_separate" if args.separate else "")
@@ -859,6 +930,10 @@ def main():
     if args.record_counters:
         # no GPU work: summarize the profiler output of earlier runs of this bench
         print(record_counters(args, cfg))
+        return
+    if args.record_patterns:
+        # no GPU work: summarize the kernel trace of an earlier --patterns-only run
+        print(record_patterns(args, cfg))
         return
     if args.record_traffic:
         # no GPU work: summarize the profiler output of an earlier run of this bench
@@ -1041,8 +1116,12 @@ def main():
     print(f"# main: {ms * 1e3:.1f} us/step  " +
           "  ".join(f"{k} {v['us']:.1f}" for k, v in out["kernels"].items()) + " us", file=sys.stderr, flush=True)
 
-    if not args.no_extras and fused and not (args.ll or args.dedup) and cfg.H % 1024 == 0 and cfg.k <= 8:
+    if (args.patterns_only or not args.no_extras) and fused and not (args.ll or args.dedup) and \
+            cfg.H % 1024 == 0 and cfg.k <= 8:
         pf = pattern_floors(torch, ep, steps, sets, K, W, d_bytes, c_bytes, N)
+        if args.patterns_only:
+            print(json.dumps(pf))
+            return
         out["access_pattern_floors"] = pf
         print(f"# access patterns: combine {pf['combine']['us']:.1f} us vs gather {pf['gather_capped']['us']:.1f}"
               + (f"; layout+dispatch {pf['layout_dispatch']['us']:.1f} us vs push {pf['push']['us']:.1f}; "
